@@ -1,0 +1,226 @@
+#!/usr/bin/env python3
+"""Benchmark of the MoE routing -> FP8 dispatch -> BF16 combine path on one
+MI355X.
+
+One step = ep_route + ep_get_layout + ep_dispatch (FP8 E4M3, 1x128 scales)
++ ep_combine over one batch of seeded synthetic input already resident in
+HBM (4096 tokens x 7168 hidden, 256 experts in 8 groups, top-4 groups,
+top-8 experts, 32 virtual ranks by default).  Expert outputs for the combine
+are a resident synthetic buffer (the expert computation is not part of the
+path).
+
+Prints one JSON line.  `value` is dispatch+combine algorithmic bytes divided
+by the summed average durations of the dispatch and combine kernels, from
+HIP events recorded on the launch stream over the timed steps.  The
+`roofline` object reports the dominant kernel (combine); `cpu_baseline`
+times the single-threaded CPU oracle on the same batch.
+
+usage: python bench.py [--gpus 1] [--steps 20] [--warmup 5]
+                       [--config prefill] [--flush] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="prefill")
+    ap.add_argument("--flush", action="store_true",
+                    help="write a 1 GiB buffer before each step so no input is cached (not timed)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(--gpus %d requested)" % args.gpus, file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import combine_group_limited_amd as ep
+    from combine_group_limited_amd import _lib as L
+    import workloads as W
+
+    w = W.CONFIGS[args.config]
+    cfg = ep.Config.of(w)
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+
+    # resident inputs
+    lg_np, x_np, y_np = W.gen_logits(w), W.gen_x(w), W.gen_y(w)
+    logits = torch.from_numpy(lg_np).to(dev)
+    x = torch.from_numpy(x_np.view(np.int16)).view(torch.bfloat16).to(dev)
+    y = torch.from_numpy(y_np.view(np.int16)).view(torch.bfloat16).to(dev)
+    i32 = dict(dtype=torch.int32, device=dev)
+    idx = torch.empty((w.T, w.k), **i32)
+    wt = torch.empty((w.T, w.k), dtype=torch.float32, device=dev)
+    cnt, ntok, off = torch.empty(w.E, **i32), torch.empty(w.R, **i32), torch.empty(w.E + 1, **i32)
+    slot, recv_token = torch.empty((w.T, w.k), **i32), torch.empty(w.nrows, **i32)
+    ws = torch.empty(max(16, ep.layout_workspace_bytes(cfg)), dtype=torch.uint8, device=dev)
+    recv = torch.empty((w.nrows, w.H), dtype=torch.uint8, device=dev)
+    scales = torch.empty((w.nrows, w.H // 128), dtype=torch.float32, device=dev)
+    out = torch.empty((w.T, w.H), dtype=torch.bfloat16, device=dev)
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev) if args.flush else None
+
+    stream = torch.cuda.current_stream(dev)
+    sh = int(stream.cuda_stream)
+    lib = L.lib()
+    c = cfg.c()
+    cp = ctypes.byref(c)
+    p = lambda t: t.data_ptr()  # noqa: E731
+    # validate once through the checked binding, then call the C ABI directly
+    ep.route(cfg, logits, idx, wt)
+    ep.get_layout(cfg, idx, dict(cnt=cnt, ntok_rank=ntok, off=off, slot=slot, recv_token=recv_token), ws)
+    ep.dispatch(cfg, x, slot, "fp8", recv, scales)
+    ep.combine(cfg, y, slot, wt, out)
+    torch.cuda.synchronize()
+
+    def check(rc, name):
+        if rc != 0:
+            raise RuntimeError("%s failed: %s" % (name, lib.ep_strerror(rc).decode()))
+
+    stages = ("route", "layout", "dispatch", "combine")
+
+    def step(ev):
+        if flush is not None:
+            flush.fill_(1)
+        ev[0].record(stream)
+        check(lib.ep_route(cp, p(logits), p(idx), p(wt), sh), "ep_route")
+        ev[1].record(stream)
+        check(lib.ep_get_layout(cp, p(idx), p(cnt), p(ntok), p(off), p(slot), p(recv_token), p(ws),
+                                ws.numel(), sh), "ep_get_layout")
+        ev[2].record(stream)
+        check(lib.ep_dispatch(cp, p(x), p(slot), L.EP_RECV_FP8_E4M3, p(recv), p(scales), sh), "ep_dispatch")
+        ev[3].record(stream)
+        check(lib.ep_combine(cp, p(y), p(slot), p(wt), p(out), sh), "ep_combine")
+        ev[4].record(stream)
+
+    mk = lambda: [torch.cuda.Event(enable_timing=True) for _ in range(5)]  # noqa: E731
+    for _ in range(args.warmup):
+        step(mk())
+    torch.cuda.synchronize()
+
+    evs = [mk() for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for ev in evs:
+        step(ev)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    dur = {s: [] for s in stages}
+    for ev in evs:
+        for i, s in enumerate(stages):
+            dur[s].append(ev[i].elapsed_time(ev[i + 1]) * 1e-3)  # seconds
+    avg = {s: float(np.mean(v)) for s, v in dur.items()}
+    med = {s: float(np.median(v)) for s, v in dur.items()}
+
+    bytes_ = dict(route=w.bytes_route(), layout=w.bytes_layout(), dispatch=w.bytes_dispatch_fp8(),
+                  combine=w.bytes_combine())
+    dc_bytes = bytes_["dispatch"] + bytes_["combine"]
+    dc_time = avg["dispatch"] + avg["combine"]
+    value = dc_bytes / dc_time / 1e9
+    per_kernel = {s: dict(avg_us=avg[s] * 1e6, median_us=med[s] * 1e6,
+                          algorithmic_bytes=bytes_[s], gbs=bytes_[s] / avg[s] / 1e9,
+                          frac=bytes_[s] / avg[s] / 1e9 / HBM_PEAK_GBS) for s in stages}
+
+    traffic = None
+    tfile = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles", "combine_prefill_traffic.json")
+    if os.path.exists(tfile) and args.config == "prefill":
+        with open(tfile) as f:
+            tr = json.load(f)
+        if tr.get("kernel_source_sha") == _kernel_sha():
+            traffic = tr.get("traffic_bytes")
+
+    comb_gbs = bytes_["combine"] / avg["combine"] / 1e9
+    rec = {
+        "metric": "dispatch+combine HBM GB/s and % of peak at 4096 tok x 7168 hidden top-8",
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall / args.steps * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "tokens": w.T, "hidden": w.H, "experts": w.E, "groups": w.G,
+                   "topk_groups": w.TG, "topk": w.k, "virtual_ranks": w.R,
+                   "dispatch": "fp8_e4m3_1x128_fp32_scales", "combine": "bf16_fp32_accumulate",
+                   "flush_between_steps": bool(args.flush)},
+        "frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4),
+        "dispatch_combine_us": round(dc_time * 1e6, 2),
+        "tokens_per_s": round(w.T / dc_time, 1),
+        "step_tokens_per_s": round(w.T / (wall / args.steps), 1),
+        "roofline": {"kernel": "combine", "bound": "hbm", "achieved": round(comb_gbs, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(comb_gbs / HBM_PEAK_GBS, 4),
+                     "traffic": traffic},
+        "kernels": {s: {k2: (round(v, 4) if isinstance(v, float) else v) for k2, v in d.items()}
+                    for s, d in per_kernel.items()},
+    }
+
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(w, lg_np, x_np, y_np, args.cpu_seconds)
+
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
+def _kernel_sha() -> str:
+    import hashlib
+    root = os.path.dirname(os.path.abspath(__file__))
+    h = hashlib.sha256()
+    for f in ("combine.hip", "device.h", "launch.h"):
+        with open(os.path.join(root, "combine_group_limited_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def cpu_baseline(w, lg, x, y, seconds: float):
+    """The CPU oracle (plain single-threaded C) on the same batch: route and
+    layout once, then FP8 dispatch + combine passes over the whole batch,
+    repeated until `seconds` of CPU time have elapsed (at most 8 passes)."""
+    import numpy as np
+
+    import oracle
+
+    idx, wt = oracle.route(lg, w.G, w.TG, w.k, w.topm)
+    lay = oracle.layout(idx, w.E, w.R)
+    q = np.empty((w.nrows, w.H), np.uint8)
+    sc = np.empty((w.nrows, w.H // 128), np.float32)
+    times = []
+    t_start = time.perf_counter()
+    while True:
+        t0 = time.perf_counter()
+        oracle.dispatch_fp8(x, lay["slot"], w.nrows, q, sc)
+        oracle.combine(y, lay["slot"], wt)
+        times.append(time.perf_counter() - t0)
+        if time.perf_counter() - t_start >= seconds or len(times) >= 8:
+            break
+    t = float(np.median(times))
+    return {"value": round((w.bytes_dispatch_fp8() + w.bytes_combine()) / t / 1e9, 4), "unit": "GB/s",
+            "cores": 1, "kind": "oracle",
+            "sample": "full %s batch (%d tokens), FP8 dispatch + combine, median of %d passes, %.2f s each"
+                      % (w.name, w.T, len(times), t)}
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,16 @@
+"""MI355X-native MoE routing, dispatch and combine (one GPU's share).
+
+The computation lives in libep.so (hand-written HIP kernels for gfx950
+behind the C ABI of include/ep.h); this package is its Python binding.
+"""
+from ._lib import EXPORTS, LIB_PATH, lib  # noqa: F401
+from .api import (  # noqa: F401
+    Config,
+    EpError,
+    combine,
+    dispatch,
+    get_layout,
+    layout_workspace_bytes,
+    route,
+    validate,
+)

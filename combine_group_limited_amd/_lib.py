@@ -1,0 +1,92 @@
+"""ctypes loader for libep.so (the C ABI of include/ep.h).
+
+torch is imported first so that the HIP runtime torch ships is the one in
+the process; libep.so links libamdhip64.so.7 by SONAME and binds to it.
+If libep.so is missing it is built with hipcc; if it cannot be loaded the
+import fails: there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+import torch  # noqa: F401  (loads torch's HIP runtime before libep.so)
+
+from . import build as _build
+
+LIB_PATH = _build.LIB_PATH
+
+EP_OK = 0
+EP_ERR_INVALID_ARG = -1
+EP_ERR_ALIGNMENT = -2
+EP_ERR_UNSUPPORTED = -3
+EP_ERR_WORKSPACE = -4
+EP_ERR_HIP = -5
+
+EP_RECV_FP8_E4M3 = 0
+EP_RECV_BF16 = 1
+
+# every function include/ep.h declares
+EXPORTS = (
+    "ep_abi_version",
+    "ep_strerror",
+    "ep_last_hip_error",
+    "ep_validate_config",
+    "ep_route",
+    "ep_layout_workspace_bytes",
+    "ep_get_layout",
+    "ep_dispatch",
+    "ep_combine",
+)
+
+
+class EpConfig(ctypes.Structure):
+    _fields_ = [
+        ("num_tokens", ctypes.c_int32),
+        ("hidden", ctypes.c_int32),
+        ("num_experts", ctypes.c_int32),
+        ("num_groups", ctypes.c_int32),
+        ("topk_groups", ctypes.c_int32),
+        ("topk", ctypes.c_int32),
+        ("num_ranks", ctypes.c_int32),
+        ("group_score_topm", ctypes.c_int32),
+    ]
+
+
+_lock = threading.Lock()
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libep.so with argument types declared."""
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(LIB_PATH):
+            _build.build()
+        L = ctypes.CDLL(LIB_PATH)
+        P = ctypes.c_void_p
+        C = ctypes.POINTER(EpConfig)
+        I = ctypes.c_int
+        L.ep_abi_version.argtypes = []
+        L.ep_abi_version.restype = I
+        L.ep_strerror.argtypes = [I]
+        L.ep_strerror.restype = ctypes.c_char_p
+        L.ep_last_hip_error.argtypes = []
+        L.ep_last_hip_error.restype = I
+        L.ep_validate_config.argtypes = [C]
+        L.ep_validate_config.restype = I
+        L.ep_route.argtypes = [C, P, P, P, P]
+        L.ep_route.restype = I
+        L.ep_layout_workspace_bytes.argtypes = [C]
+        L.ep_layout_workspace_bytes.restype = ctypes.c_size_t
+        L.ep_get_layout.argtypes = [C, P, P, P, P, P, P, P, ctypes.c_size_t, P]
+        L.ep_get_layout.restype = I
+        L.ep_dispatch.argtypes = [C, P, P, I, P, P, P]
+        L.ep_dispatch.restype = I
+        L.ep_combine.argtypes = [C, P, P, P, P, P]
+        L.ep_combine.restype = I
+        _lib = L
+        return _lib

@@ -1,0 +1,145 @@
+// api.hip -- the C ABI declared in include/ep.h: validation, error codes and
+// kernel launches.  No HIP call happens before validation succeeds; nothing
+// here allocates or synchronises.
+#include <hip/hip_runtime.h>
+
+#include <stdint.h>
+
+#include "ep.h"
+#include "launch.h"
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+constexpr int32_t kMaxTokens = 1 << 24;
+constexpr int32_t kMaxHidden = 16384;
+constexpr int32_t kMaxExperts = 1024;
+constexpr int32_t kMaxGroups = 64;
+constexpr int32_t kMaxTopk = 32;
+constexpr int32_t kMaxTopm = 8;
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+int effective_topm(const ep_config_t* c) {
+    if (c->group_score_topm != 0) return c->group_score_topm;
+    const int m = c->topk / c->topk_groups;
+    return m > 0 ? m : 1;
+}
+
+int validate(const ep_config_t* c) {
+    if (!c) return EP_ERR_INVALID_ARG;
+    const ep_config_t& v = *c;
+    if (v.num_tokens < 0 || v.hidden < 128 || v.hidden % 128 != 0) return EP_ERR_INVALID_ARG;
+    if (v.num_experts < 1 || v.num_groups < 1 || v.num_experts % v.num_groups != 0) return EP_ERR_INVALID_ARG;
+    if (v.topk_groups < 1 || v.topk_groups > v.num_groups) return EP_ERR_INVALID_ARG;
+    const int gs = v.num_experts / v.num_groups;
+    if (v.topk < 1 || (long)v.topk > (long)v.topk_groups * gs) return EP_ERR_INVALID_ARG;
+    if (v.num_ranks < 1 || v.num_experts % v.num_ranks != 0) return EP_ERR_INVALID_ARG;
+    if (v.group_score_topm < 0) return EP_ERR_INVALID_ARG;
+    const int m = effective_topm(c);
+    if (m > gs) return EP_ERR_INVALID_ARG;
+    if ((long)v.num_tokens * v.topk >= (1L << 31)) return EP_ERR_INVALID_ARG;
+    if (v.num_tokens > kMaxTokens || v.hidden > kMaxHidden || v.num_experts > kMaxExperts ||
+        v.num_groups > kMaxGroups || v.topk > kMaxTopk || m > kMaxTopm)
+        return EP_ERR_UNSUPPORTED;
+    return EP_OK;
+}
+
+ep::Shape shape_of(const ep_config_t* c) {
+    return ep::Shape{c->num_tokens, c->hidden,    c->num_experts, c->num_groups,
+                     c->topk_groups, c->topk, c->num_ranks,   effective_topm(c)};
+}
+
+int hip_status(hipError_t e) {
+    if (e == hipSuccess) return EP_OK;
+    g_last_hip_error = (int)e;
+    return EP_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+EP_API int ep_abi_version(void) { return EP_ABI_VERSION; }
+
+EP_API const char* ep_strerror(int code) {
+    switch (code) {
+        case EP_OK: return "success";
+        case EP_ERR_INVALID_ARG: return "invalid argument (null pointer or inconsistent sizes)";
+        case EP_ERR_ALIGNMENT: return "pointer not aligned as required";
+        case EP_ERR_UNSUPPORTED: return "configuration outside the kernels' supported limits";
+        case EP_ERR_WORKSPACE: return "workspace missing or too small";
+        case EP_ERR_HIP: return "HIP kernel launch failed (see ep_last_hip_error)";
+        default: return "unknown error code";
+    }
+}
+
+EP_API int ep_last_hip_error(void) { return g_last_hip_error; }
+
+EP_API int ep_validate_config(const ep_config_t* cfg) { return validate(cfg); }
+
+EP_API int ep_route(const ep_config_t* cfg, const float* logits, int32_t* topk_idx, float* topk_w,
+                    void* stream) {
+    int rc = validate(cfg);
+    if (rc) return rc;
+    if (cfg->num_tokens > 0 && (!logits || !topk_idx || !topk_w)) return EP_ERR_INVALID_ARG;
+    if (!aligned(logits, 4) || !aligned(topk_idx, 4) || !aligned(topk_w, 4)) return EP_ERR_ALIGNMENT;
+    return hip_status(ep::launch_route(shape_of(cfg), logits, topk_idx, topk_w,
+                                       static_cast<hipStream_t>(stream)));
+}
+
+EP_API size_t ep_layout_workspace_bytes(const ep_config_t* cfg) {
+    if (validate(cfg)) return 0;
+    return ep::layout_workspace_bytes(shape_of(cfg));
+}
+
+EP_API int ep_get_layout(const ep_config_t* cfg, const int32_t* topk_idx, int32_t* cnt_expert,
+                         int32_t* ntok_rank, int32_t* expert_offset, int32_t* slot, int32_t* recv_token,
+                         void* workspace, size_t workspace_bytes, void* stream) {
+    int rc = validate(cfg);
+    if (rc) return rc;
+    if (!cnt_expert || !ntok_rank || !expert_offset) return EP_ERR_INVALID_ARG;
+    if (cfg->num_tokens > 0 && (!topk_idx || !slot)) return EP_ERR_INVALID_ARG;
+    if (!aligned(topk_idx, 4) || !aligned(cnt_expert, 4) || !aligned(ntok_rank, 4) ||
+        !aligned(expert_offset, 4) || !aligned(slot, 4) || !aligned(recv_token, 4))
+        return EP_ERR_ALIGNMENT;
+    const ep::Shape s = shape_of(cfg);
+    const size_t need = ep::layout_workspace_bytes(s);
+    if (need > 0 && (!workspace || workspace_bytes < need)) return EP_ERR_WORKSPACE;
+    if (!aligned(workspace, 16)) return EP_ERR_ALIGNMENT;
+    return hip_status(ep::launch_layout(s, topk_idx, cnt_expert, ntok_rank, expert_offset, slot, recv_token,
+                                        workspace, static_cast<hipStream_t>(stream)));
+}
+
+EP_API int ep_dispatch(const ep_config_t* cfg, const void* x, const int32_t* slot, int recv_dtype, void* recv,
+                       float* recv_scales, void* stream) {
+    int rc = validate(cfg);
+    if (rc) return rc;
+    if (recv_dtype != EP_RECV_FP8_E4M3 && recv_dtype != EP_RECV_BF16) return EP_ERR_INVALID_ARG;
+    const bool fp8 = recv_dtype == EP_RECV_FP8_E4M3;
+    if (cfg->num_tokens > 0 && (!x || !slot || !recv || (fp8 && !recv_scales))) return EP_ERR_INVALID_ARG;
+    if (!fp8 && recv_scales) return EP_ERR_INVALID_ARG;
+    if (!aligned(x, 16) || !aligned(recv, 16) || !aligned(slot, 4) || !aligned(recv_scales, 4))
+        return EP_ERR_ALIGNMENT;
+    const ep::Shape s = shape_of(cfg);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (fp8)
+        return hip_status(ep::launch_dispatch_fp8(s, static_cast<const uint16_t*>(x), slot,
+                                                  static_cast<uint8_t*>(recv), recv_scales, st));
+    return hip_status(ep::launch_dispatch_bf16(s, static_cast<const uint16_t*>(x), slot,
+                                               static_cast<uint16_t*>(recv), st));
+}
+
+EP_API int ep_combine(const ep_config_t* cfg, const void* y, const int32_t* slot, const float* topk_w,
+                      void* out, void* stream) {
+    int rc = validate(cfg);
+    if (rc) return rc;
+    if (cfg->num_tokens > 0 && (!y || !slot || !topk_w || !out)) return EP_ERR_INVALID_ARG;
+    if (!aligned(y, 16) || !aligned(out, 16) || !aligned(slot, 4) || !aligned(topk_w, 4))
+        return EP_ERR_ALIGNMENT;
+    return hip_status(ep::launch_combine(shape_of(cfg), static_cast<const uint16_t*>(y), slot, topk_w,
+                                         static_cast<uint16_t*>(out), static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

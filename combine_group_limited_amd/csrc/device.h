@@ -1,0 +1,85 @@
+// device.h -- gfx950 device helpers shared by the library's kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ep {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// Two fp32 -> packed bf16x2 (lo in bits 0..15), round to nearest even.
+// gfx950 converts with v_cvt_pk_bf16_f32.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    __bf16 a = (__bf16)lo;
+    __bf16 b = (__bf16)hi;
+    return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+}
+
+// Four fp32 -> four OCP E4M3 codes packed little-endian in one dword, round
+// to nearest even.  gfx950's v_cvt_pk_fp8_f32 produces the OCP encoding.
+// Callers keep |v| <= 448 * (1 + 2^-22), which rounds to at most 448.
+__device__ __forceinline__ uint32_t pack_e4m3x4(float a, float b, float c, float d) {
+    int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+    w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
+    return (uint32_t)w;
+}
+
+// exp(x), fp32, by Cody & Waite additive range reduction and a degree-7
+// Taylor polynomial in Horner form with fused multiply-add.  Constants:
+// L2E = fp32(log2 e); C1 = fp32(ln 2) with its low 12 significand bits
+// cleared (n * C1 exact); C2 = fp32(ln 2 - C1); P_i = fp32(1 / i!).  For
+// x in [-86, 88] the scale 2^n is a normal number and the final multiply is
+// exact; beyond that the result is 0 or +inf.
+__device__ __forceinline__ float cw_expf(float x) {
+    if (__builtin_isnan(x)) return x;
+    if (x > 88.0f) return __builtin_huge_valf();
+    if (x < -86.0f) return 0.0f;
+    const float L2E = 0x1.715476p+0f;
+    const float C1 = 0x1.62ep-1f;
+    const float C2 = 0x1.0bfbe8p-15f;
+    float n = __builtin_rintf(x * L2E);
+    float r = __builtin_fmaf(-n, C1, x);
+    r = __builtin_fmaf(-n, C2, r);
+    float p = 0x1.a01a02p-13f;                 // 1/7!
+    p = __builtin_fmaf(p, r, 0x1.6c16c2p-10f);  // 1/6!
+    p = __builtin_fmaf(p, r, 0x1.111112p-7f);   // 1/5!
+    p = __builtin_fmaf(p, r, 0x1.555556p-5f);   // 1/4!
+    p = __builtin_fmaf(p, r, 0x1.555556p-3f);   // 1/3!
+    p = __builtin_fmaf(p, r, 0.5f);             // 1/2!
+    p = __builtin_fmaf(p, r, 1.0f);             // 1/1!
+    p = __builtin_fmaf(p, r, 1.0f);             // 1/0!
+    return p * __uint_as_float((uint32_t)((int)n + 127) << 23);
+}
+
+__device__ __forceinline__ float sigmoid(float x) { return 1.0f / (1.0f + cw_expf(-x)); }
+
+// Largest 64-bit value across the wavefront (every lane gets it).
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) {
+        uint32_t lo = __shfl_xor((uint32_t)v, d, kWave);
+        uint32_t hi = __shfl_xor((uint32_t)(v >> 32), d, kWave);
+        uint64_t o = ((uint64_t)hi << 32) | lo;
+        v = o > v ? o : v;
+    }
+    return v;
+}
+
+// Inclusive prefix sum across the wavefront.
+__device__ __forceinline__ int wave_inclusive_sum(int v) {
+    const int lane = threadIdx.x & (kWave - 1);
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) {
+        int o = __shfl_up(v, d, kWave);
+        if (lane >= d) v += o;
+    }
+    return v;
+}
+
+}  // namespace ep

@@ -1,0 +1,126 @@
+// dispatch.hip -- scatter of each token's hidden row to its k receive rows,
+// as FP8 E4M3 with one fp32 scale per 128 channels, or as BF16.
+//
+// Dispatch sends each token to the experts its gate chose (DeepEP blog
+// "【Day2】DeepEP ...", section "DeepEP是什么"); the DeepEP test setting uses an
+// FP8 payload for dispatch (news report on the release, "具体性能方面").  The
+// scaling rule is this library's reading: per token and 128-channel block,
+// amax = max |x|, a = max(amax, 1e-4), inv = 448 / a, scale = a / 448,
+// code = e4m3_rne(x * inv).
+//
+// FP8 kernel: a lane owns 16 consecutive channels (two 16-byte loads of
+// bf16, one 16-byte store of codes per receive row), so a 128-channel block
+// is 8 adjacent lanes and its amax is a 3-step butterfly.  The row is read
+// from HBM once and written k times; receive-row indices are loaded once per
+// wavefront and broadcast with v_readlane, so each store's address is
+// wave-uniform.
+#include "device.h"
+#include "launch.h"
+
+namespace ep {
+
+namespace {
+
+__global__ __launch_bounds__(1024) void dispatch_fp8_kernel(const uint16_t* __restrict__ x,
+                                                             const int32_t* __restrict__ slot,
+                                                             uint8_t* __restrict__ recv,
+                                                             float* __restrict__ recv_sc, int H, int k,
+                                                             int nrows, int segs) {
+    const int lane = threadIdx.x & 63;
+    const int t = blockIdx.x / segs;
+    const int seg = blockIdx.x - t * segs;
+    const int chunk = seg * blockDim.x + threadIdx.x;  // 16-channel piece of row t
+    const int nchunks = H >> 4;
+
+    // receive rows of token t, one per lane j < k (loaded with all lanes on)
+    int my_slot = -1;
+    if (lane < k) my_slot = slot[(size_t)t * k + lane];
+
+    // whole 8-lane groups fall outside the row together (H % 128 == 0)
+    if (chunk < nchunks) {
+        const u32x4* src = reinterpret_cast<const u32x4*>(x + (size_t)t * H) + 2 * chunk;
+        const u32x4 a = __builtin_nontemporal_load(src);
+        const u32x4 b = __builtin_nontemporal_load(src + 1);
+        float f[16];
+        f[0] = bf16_lo(a.x);  f[1] = bf16_hi(a.x);  f[2] = bf16_lo(a.y);  f[3] = bf16_hi(a.y);
+        f[4] = bf16_lo(a.z);  f[5] = bf16_hi(a.z);  f[6] = bf16_lo(a.w);  f[7] = bf16_hi(a.w);
+        f[8] = bf16_lo(b.x);  f[9] = bf16_hi(b.x);  f[10] = bf16_lo(b.y); f[11] = bf16_hi(b.y);
+        f[12] = bf16_lo(b.z); f[13] = bf16_hi(b.z); f[14] = bf16_lo(b.w); f[15] = bf16_hi(b.w);
+
+        float amax = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(f[i]));
+        amax = fmaxf(amax, __shfl_xor(amax, 1, kWave));
+        amax = fmaxf(amax, __shfl_xor(amax, 2, kWave));
+        amax = fmaxf(amax, __shfl_xor(amax, 4, kWave));
+        const float ac = fmaxf(amax, 1e-4f);
+        const float inv = 448.0f / ac;
+        const float sc = ac / 448.0f;
+
+        u32x4 q;
+        q.x = pack_e4m3x4(f[0] * inv, f[1] * inv, f[2] * inv, f[3] * inv);
+        q.y = pack_e4m3x4(f[4] * inv, f[5] * inv, f[6] * inv, f[7] * inv);
+        q.z = pack_e4m3x4(f[8] * inv, f[9] * inv, f[10] * inv, f[11] * inv);
+        q.w = pack_e4m3x4(f[12] * inv, f[13] * inv, f[14] * inv, f[15] * inv);
+
+        const int nblk = H >> 7;
+        for (int j = 0; j < k; ++j) {
+            const int r = __builtin_amdgcn_readlane(my_slot, j);
+            if ((unsigned)r < (unsigned)nrows) {
+                u32x4* dst = reinterpret_cast<u32x4*>(recv + (size_t)r * H) + chunk;
+                __builtin_nontemporal_store(q, dst);
+                if ((lane & 7) == 0) recv_sc[(size_t)r * nblk + (chunk >> 3)] = sc;
+            }
+        }
+    }
+}
+
+// BF16: a lane owns 8 channels (one 16-byte load, one 16-byte store per row).
+__global__ __launch_bounds__(1024) void dispatch_bf16_kernel(const uint16_t* __restrict__ x,
+                                                              const int32_t* __restrict__ slot,
+                                                              uint16_t* __restrict__ recv, int H, int k,
+                                                              int nrows, int segs) {
+    const int lane = threadIdx.x & 63;
+    const int t = blockIdx.x / segs;
+    const int seg = blockIdx.x - t * segs;
+    const int chunk = seg * blockDim.x + threadIdx.x;  // 8-channel piece of row t
+    const int nchunks = H >> 3;
+
+    int my_slot = -1;
+    if (lane < k) my_slot = slot[(size_t)t * k + lane];
+
+    if (chunk < nchunks) {
+        const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(x + (size_t)t * H) + chunk);
+        for (int j = 0; j < k; ++j) {
+            const int r = __builtin_amdgcn_readlane(my_slot, j);
+            if ((unsigned)r < (unsigned)nrows) {
+                u32x4* dst = reinterpret_cast<u32x4*>(recv + (size_t)r * H) + chunk;
+                __builtin_nontemporal_store(v, dst);
+            }
+        }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_dispatch_fp8(const Shape& s, const uint16_t* x, const int32_t* slot, uint8_t* recv,
+                               float* recv_scales, hipStream_t stream) {
+    if (s.T == 0) return hipSuccess;
+    const RowGeometry g = row_geometry(s.T, s.H >> 4);
+    const long blocks = (long)s.T * g.segs;
+    hipLaunchKernelGGL(dispatch_fp8_kernel, dim3((unsigned)blocks), dim3(g.threads), 0, stream, x, slot,
+                       recv, recv_scales, s.H, s.k, s.T * s.k, g.segs);
+    return hipGetLastError();
+}
+
+hipError_t launch_dispatch_bf16(const Shape& s, const uint16_t* x, const int32_t* slot, uint16_t* recv,
+                                hipStream_t stream) {
+    if (s.T == 0) return hipSuccess;
+    const RowGeometry g = row_geometry(s.T, s.H >> 3);
+    const long blocks = (long)s.T * g.segs;
+    hipLaunchKernelGGL(dispatch_bf16_kernel, dim3((unsigned)blocks), dim3(g.threads), 0, stream, x, slot,
+                       recv, s.H, s.k, s.T * s.k, g.segs);
+    return hipGetLastError();
+}
+
+}  // namespace ep

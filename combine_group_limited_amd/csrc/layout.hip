@@ -1,0 +1,226 @@
+// layout.hip -- routing layout: per-expert counts and offsets, per-rank
+// token counts, and the canonical token -> receive-row map.
+//
+// The DeepEP blog "【Day2】DeepEP ..." (caption in "DeepEP是什么") has the host
+// wait for the GPU's receive counts; here the receive buffer is statically
+// T*k rows, so the counts stay on the device and nothing waits.
+//
+// Row order: one row per routed (token, expert) pair, grouped by expert,
+// pairs in row-major (t, j) order within an expert.  The order is computed
+// without order-dependent atomics, so the result is deterministic:
+//   count  (C blocks)      per-block expert histograms and per-block counts
+//                          of tokens per virtual rank (LDS atomic adds)
+//   scan   (E + R blocks)  per-expert exclusive scan of the block
+//                          histograms; per-rank totals
+//   assign (C blocks)      expert offsets by a block-wide scan, then each
+//                          wavefront sets one bit per pair in an LDS mask per
+//                          expert (atomic OR commutes); a pair's rank inside
+//                          its wavefront is the popcount of the mask bits of
+//                          the lanes before it
+// Workspace: hist [E][C] and rank counts [R][C], int32, C = ceil(T*k / P)
+// with P = 64 * waves-per-block pairs per block.
+#include "device.h"
+#include "launch.h"
+
+namespace ep {
+
+namespace {
+
+constexpr int kScanThreads = 256;
+
+// waves per block of the count/assign kernels; the assign kernel needs
+// (12 * W + 4) * E bytes of LDS
+inline int layout_waves(int E) { return (100 * E <= 65536) ? 8 : 4; }
+
+inline int layout_blocks(long P, int W) { return (int)((P + 64 * W - 1) / (64 * W)); }
+
+// exclusive block-wide prefix sum; `wsum` is LDS scratch of blockDim/64 ints
+__device__ int block_exclusive_sum(int v, int* total, int* wsum) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+    const int inc = wave_inclusive_sum(v);
+    if (lane == 63) wsum[wave] = inc;
+    __syncthreads();
+    int pre = 0, tot = 0;
+    for (int w = 0; w < nw; ++w) {
+        const int x = wsum[w];
+        pre += (w < wave) ? x : 0;
+        tot += x;
+    }
+    __syncthreads();
+    *total = tot;
+    return pre + inc - v;
+}
+
+__global__ __launch_bounds__(512) void layout_count_kernel(const int32_t* __restrict__ idx,
+                                                           int32_t* __restrict__ hist,
+                                                           int32_t* __restrict__ rk, long P, int k, int E,
+                                                           int R, int EPR, int C) {
+    extern __shared__ int32_t cnt_sm[];  // E expert counts, then R rank counts
+    const int tid = threadIdx.x;
+    for (int i = tid; i < E + R; i += blockDim.x) cnt_sm[i] = 0;
+    __syncthreads();
+    const long p = (long)blockIdx.x * blockDim.x + tid;
+    if (p < P) {
+        const int e = idx[p];
+        if ((unsigned)e < (unsigned)E) {
+            atomicAdd(&cnt_sm[e], 1);
+            // a token counts once per rank: only its first pair on the rank adds
+            const int r = e / EPR;
+            const long t = p / k;
+            const int j = (int)(p - t * k);
+            bool first = true;
+            for (int jj = 0; jj < j; ++jj) {
+                const int e2 = idx[t * k + jj];
+                if ((unsigned)e2 < (unsigned)E && e2 / EPR == r) first = false;
+            }
+            if (first) atomicAdd(&cnt_sm[E + r], 1);
+        }
+    }
+    __syncthreads();
+    const int c = blockIdx.x;
+    for (int i = tid; i < E; i += blockDim.x) hist[(size_t)i * C + c] = cnt_sm[i];
+    for (int i = tid; i < R; i += blockDim.x) rk[(size_t)i * C + c] = cnt_sm[E + i];
+}
+
+// block b < E: exclusive scan of hist[b][0..C) in place, cnt[b] = total;
+// block E + r: ntok_rank[r] = sum of rk[r][0..C)
+__global__ __launch_bounds__(kScanThreads) void layout_scan_kernel(int32_t* __restrict__ hist,
+                                                                   const int32_t* __restrict__ rk,
+                                                                   int32_t* __restrict__ cnt,
+                                                                   int32_t* __restrict__ ntok_rank, int E,
+                                                                   int C) {
+    __shared__ int wsum[kScanThreads / 64];
+    const int b = blockIdx.x;
+    const int tid = threadIdx.x;
+    if (b < E) {
+        int32_t* col = hist + (size_t)b * C;
+        int carry = 0;
+        for (int c0 = 0; c0 < C; c0 += kScanThreads) {
+            const int c = c0 + tid;
+            const int v = (c < C) ? col[c] : 0;
+            int tile;
+            const int ex = block_exclusive_sum(v, &tile, wsum);
+            if (c < C) col[c] = carry + ex;
+            carry += tile;
+        }
+        if (tid == 0) cnt[b] = carry;
+    } else {
+        const int32_t* row = rk + (size_t)(b - E) * C;
+        int sum = 0;
+        for (int c0 = 0; c0 < C; c0 += kScanThreads) {
+            const int c = c0 + tid;
+            const int v = (c < C) ? row[c] : 0;
+            int tile;
+            block_exclusive_sum(v, &tile, wsum);
+            sum += tile;
+        }
+        if (tid == 0) ntok_rank[b - E] = sum;
+    }
+}
+
+template <int W>
+__global__ __launch_bounds__(W * 64) void layout_assign_kernel(
+    const int32_t* __restrict__ idx, const int32_t* __restrict__ hist, const int32_t* __restrict__ cnt,
+    int32_t* __restrict__ off, int32_t* __restrict__ slot, int32_t* __restrict__ recv_token, long P,
+    int k, int E, int C) {
+    extern __shared__ __align__(16) unsigned char asg_sm[];
+    uint64_t* mask = reinterpret_cast<uint64_t*>(asg_sm);       // [W][E]
+    int32_t* wpre = reinterpret_cast<int32_t*>(mask + W * E);    // [W][E]
+    int32_t* base = wpre + W * E;                                // [E]
+    __shared__ int wsum[W];
+
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int c = blockIdx.x;
+    constexpr int NT = W * 64;
+
+    for (int i = tid; i < W * E; i += NT) mask[i] = 0ull;
+
+    // expert offsets: each thread scans EPT consecutive experts
+    const int EPT = (E + NT - 1) / NT;
+    const int e0 = tid * EPT;
+    int local = 0;
+    for (int i = 0; i < EPT; ++i)
+        if (e0 + i < E) local += cnt[e0 + i];
+    int total;
+    int ex = block_exclusive_sum(local, &total, wsum);
+    for (int i = 0; i < EPT; ++i) {
+        const int e = e0 + i;
+        if (e < E) {
+            base[e] = ex + ((c < C) ? hist[(size_t)e * C + c] : 0);
+            if (c == 0) off[e] = ex;
+            ex += cnt[e];
+        }
+    }
+    if (c == 0 && tid == 0) off[E] = total;
+
+    const long p = (long)c * NT + tid;
+    int e = -1;
+    if (p < P) {
+        const int v = idx[p];
+        if ((unsigned)v < (unsigned)E) e = v;
+    }
+    __syncthreads();
+    if (e >= 0) atomicOr(reinterpret_cast<unsigned long long*>(&mask[wave * E + e]), 1ull << lane);
+    __syncthreads();
+    for (int i = tid; i < E; i += NT) {
+        int run = 0;
+        for (int w = 0; w < W; ++w) {
+            wpre[w * E + i] = run;
+            run += __popcll(mask[w * E + i]);
+        }
+    }
+    __syncthreads();
+    if (p < P) {
+        int s = -1;
+        if (e >= 0) {
+            const uint64_t before = mask[wave * E + e] & ((1ull << lane) - 1ull);
+            s = base[e] + wpre[wave * E + e] + __popcll(before);
+            if (recv_token) recv_token[s] = (int32_t)(p / k);
+        }
+        slot[p] = s;
+        if (recv_token && p >= total) recv_token[p] = -1;
+    }
+}
+
+template <int W>
+hipError_t launch_assign(const Shape& s, long P, int C, const int32_t* idx, const int32_t* hist,
+                         const int32_t* cnt, int32_t* off, int32_t* slot, int32_t* recv_token,
+                         hipStream_t st) {
+    const size_t lds = (size_t)(12 * W + 4) * s.E;
+    const int blocks = C > 0 ? C : 1;  // block 0 writes the offsets even with no pairs
+    hipLaunchKernelGGL(layout_assign_kernel<W>, dim3(blocks), dim3(W * 64), lds, st, idx, hist, cnt, off,
+                       slot, recv_token, P, s.k, s.E, C);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+size_t layout_workspace_bytes(const Shape& s) {
+    const long P = (long)s.T * s.k;
+    const int C = layout_blocks(P, layout_waves(s.E));
+    const size_t b = (size_t)(s.E + s.R) * (size_t)C * sizeof(int32_t);
+    return (b + 255) & ~(size_t)255;
+}
+
+hipError_t launch_layout(const Shape& s, const int32_t* topk_idx, int32_t* cnt, int32_t* ntok_rank,
+                         int32_t* off, int32_t* slot, int32_t* recv_token, void* ws, hipStream_t stream) {
+    const long P = (long)s.T * s.k;
+    const int W = layout_waves(s.E);
+    const int C = layout_blocks(P, W);
+    int32_t* hist = static_cast<int32_t*>(ws);
+    int32_t* rk = hist + (size_t)s.E * C;
+    if (C > 0) {
+        hipLaunchKernelGGL(layout_count_kernel, dim3(C), dim3(W * 64), (size_t)(s.E + s.R) * sizeof(int32_t),
+                           stream, topk_idx, hist, rk, P, s.k, s.E, s.R, s.E / s.R, C);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL(layout_scan_kernel, dim3(s.E + s.R), dim3(kScanThreads), 0, stream, hist, rk, cnt,
+                       ntok_rank, s.E, C);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    if (W == 8) return launch_assign<8>(s, P, C, topk_idx, hist, cnt, off, slot, recv_token, stream);
+    return launch_assign<4>(s, P, C, topk_idx, hist, cnt, off, slot, recv_token, stream);
+}
+
+}  // namespace ep

@@ -1,0 +1,192 @@
+/*
+ * ep.h -- C ABI of the MI355X (gfx950) MoE routing, dispatch and combine
+ * library (libep.so).
+ *
+ * The library computes, on one GPU, the data-parallel core of expert-
+ * parallel MoE communication as the DeepEP pages describe it:
+ *   ep_route       group-limited top-k gating
+ *   ep_get_layout  per-expert and per-rank receive counts, offsets, slots
+ *   ep_dispatch    scatter of each token to its k experts' receive rows,
+ *                  FP8 (E4M3 + fp32 scale per 128 channels) or BF16
+ *   ep_combine     gather of each token's k expert outputs, weighted sum
+ * Sources (titles of the pages, then the section):
+ *   [NEWS]  news report on the DeepEP release (yunnanlong.com): feature list;
+ *           "具体性能方面" (test settings: FP8 dispatch, BF16 combine)
+ *   [DAY2]  blog "【Day2】DeepEP - 第一个用于 MoE 模型训练和推理的开源 EP 通信库":
+ *           "DeepEP是什么" (dispatch and combine; the host waits for the
+ *           receive count), "All-to-All通信" (combine accumulates),
+ *           "DeepEP的关键技术" (native FP8 dispatch)
+ *   [DE]    German summary page "DeepEP" (flashmla.org): group-limited gating
+ * The pages print no formulas; every arithmetic rule below is the reading
+ * this library implements and states.
+ *
+ * Expert parallelism is emulated on one GPU: virtual rank r owns experts
+ * [r*E/R, (r+1)*E/R), and the receive buffers of all ranks are one buffer of
+ * T*k rows ordered by expert, so rank r's rows start at expert_offset[r*E/R].
+ *
+ * Conventions for every call
+ *  - Pointers named as device pointers must point to GPU memory (for
+ *    example torch tensors) that stays alive until the work enqueued on
+ *    `stream` has finished.  `cfg` is a host pointer read during the call.
+ *  - `stream` is a hipStream_t (NULL = the null stream).  Calls only enqueue
+ *    kernels and return; they never synchronise and never allocate.
+ *  - Arrays are dense and row-major.  bf16 data is 16-bit brain float,
+ *    fp8 data is OCP OFP8 E4M3 ("e4m3fn": max 448, no infinities).
+ *  - Inputs are read-only.  Outputs are written in full unless stated
+ *    otherwise, so callers need not clear them.  Inputs and outputs must not
+ *    overlap.
+ *  - Errors: negative return codes (below); validation happens before any
+ *    HIP call, so an invalid call has no effect.  EP_ERR_HIP reports a
+ *    failed kernel launch (ep_last_hip_error gives the hipError_t).
+ *    Faults inside kernels surface as HIP errors at the caller's next
+ *    synchronisation, as for any HIP kernel.
+ *  - Calls are reentrant and keep no state between calls.
+ */
+#ifndef EP_H
+#define EP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define EP_API __attribute__((visibility("default")))
+
+#define EP_ABI_VERSION 1
+
+/* Return codes */
+#define EP_OK               0
+#define EP_ERR_INVALID_ARG (-1)  /* null pointer, inconsistent sizes       */
+#define EP_ERR_ALIGNMENT   (-2)  /* pointer not aligned as required        */
+#define EP_ERR_UNSUPPORTED (-3)  /* valid, but outside the kernels' limits */
+#define EP_ERR_WORKSPACE   (-4)  /* workspace missing or too small         */
+#define EP_ERR_HIP         (-5)  /* a kernel launch failed                 */
+
+/* Receive payload types for ep_dispatch */
+#define EP_RECV_FP8_E4M3 0
+#define EP_RECV_BF16     1
+
+/* Problem description shared by all calls.
+ *   num_tokens        T, 0 <= T <= 2^24, with T * topk < 2^31
+ *   hidden            H, a multiple of 128, 128 <= H <= 16384
+ *   num_experts       E, 1 <= E <= 1024
+ *   num_groups        G, divides E, 1 <= G <= 64
+ *   topk_groups       TG, 1 <= TG <= G
+ *   topk              k, 1 <= k <= 32 and k <= TG * E / G
+ *   num_ranks         R, divides E
+ *   group_score_topm  m, the number of best scores summed into a group's
+ *                     score; 0 selects max(1, k / TG); 1 <= m <= min(8, E/G)
+ */
+typedef struct ep_config {
+    int32_t num_tokens;
+    int32_t hidden;
+    int32_t num_experts;
+    int32_t num_groups;
+    int32_t topk_groups;
+    int32_t topk;
+    int32_t num_ranks;
+    int32_t group_score_topm;
+} ep_config_t;
+
+/* EP_ABI_VERSION of the built library. */
+EP_API int ep_abi_version(void);
+
+/* Static, NUL-terminated description of a return code. */
+EP_API const char* ep_strerror(int code);
+
+/* The hipError_t of the last failed launch seen by this library on the
+ * calling thread (0 if none). */
+EP_API int ep_last_hip_error(void);
+
+/* EP_OK if `cfg` satisfies the limits above, else the error code any call
+ * would return for it. */
+EP_API int ep_validate_config(const ep_config_t* cfg);
+
+/* Group-limited top-k gating ([NEWS] feature list; [DE]).
+ *   logits    device, fp32 [T, E]
+ *   topk_idx  device, int32 [T, k]  out: chosen experts, best first
+ *   topk_w    device, fp32 [T, k]  out: gate weights, summing to one
+ * Per token: s_e = 1 / (1 + exp(-logit_e)) in fp32, exp evaluated by Cody &
+ * Waite range reduction and a degree-7 Taylor polynomial (exp(x) = +inf for
+ * x > 88, 0 for x < -86); a group's score is the sum of its m best scores,
+ * largest first; the TG best groups are kept (score desc, index asc); the k
+ * best experts of the kept groups are chosen (score desc, index asc); the
+ * weight of pick j is s_j / ((s_0 + s_1) + ... + s_{k-1}).  Scores rank by
+ * their IEEE bit pattern, which is numeric order for sigmoid's outputs.
+ * Logits must not be NaN (the selection is then unspecified, still k
+ * distinct in-range experts).
+ * Alignment: 4 bytes.  Kernel: one 64-lane wavefront per token. */
+EP_API int ep_route(const ep_config_t* cfg, const float* logits,
+                    int32_t* topk_idx, float* topk_w, void* stream);
+
+/* Bytes of device workspace ep_get_layout needs for `cfg` (0 if invalid). */
+EP_API size_t ep_layout_workspace_bytes(const ep_config_t* cfg);
+
+/* Routing layout ([DAY2] "DeepEP是什么": receive counts known before the
+ * exchange).  One receive row per routed (token, expert) pair, rows grouped
+ * by expert, tokens ascending within an expert.
+ *   topk_idx       device, int32 [T, k]; entries outside [0, E) are
+ *                  unrouted.  A token may name an expert more than once
+ *                  (ep_route never does); each occurrence gets its own row.
+ *   cnt_expert     device, int32 [E]     out: routed pairs per expert
+ *   ntok_rank      device, int32 [R]     out: tokens with >= 1 routed expert
+ *                                        on virtual rank r
+ *   expert_offset  device, int32 [E + 1] out: exclusive prefix sum of
+ *                                        cnt_expert; [E] = routed pairs
+ *   slot           device, int32 [T, k]  out: receive row of pair (t, j) =
+ *                  expert_offset[e] + number of earlier pairs (row-major
+ *                  order) with the same expert; -1 if unrouted
+ *   recv_token     device, int32 [T * k] out (may be NULL): token owning
+ *                  each receive row; -1 for rows >= expert_offset[E]
+ *   workspace      device, >= ep_layout_workspace_bytes(cfg) bytes, 16-byte
+ *                  aligned; contents need not be initialised and are
+ *                  scratch after the call
+ * The receive buffer size is T*k rows whatever the routing, so the host
+ * never has to wait for the counts.  Deterministic: counting uses
+ * commutative operations only.  Alignment: 4 bytes (workspace 16). */
+EP_API int ep_get_layout(const ep_config_t* cfg, const int32_t* topk_idx,
+                         int32_t* cnt_expert, int32_t* ntok_rank,
+                         int32_t* expert_offset, int32_t* slot,
+                         int32_t* recv_token, void* workspace,
+                         size_t workspace_bytes, void* stream);
+
+/* Dispatch ([DAY2] "DeepEP是什么"; FP8 payload: [NEWS] "具体性能方面",
+ * [DAY2] "DeepEP的关键技术").
+ *   x            device, bf16 [T, H], 16-byte aligned
+ *   slot         device, int32 [T, k] from ep_get_layout; entries outside
+ *                [0, T*k) are skipped
+ *   recv_dtype   EP_RECV_FP8_E4M3 or EP_RECV_BF16
+ *   recv         device, [T*k, H] of e4m3 codes (1 byte) or bf16, 16-byte
+ *                aligned.  Row slot[t,j] receives token t; rows no slot
+ *                names are not written.
+ *   recv_scales  device, fp32 [T*k, H/128] for FP8 (NULL for BF16), 4-byte
+ *                aligned; row slot[t,j] receives token t's scales
+ * FP8, per token and 128-channel block: amax = max |x|, a = max(amax,
+ * 1e-4), inv = 448 / a, scale = a / 448, code = e4m3(x * inv) rounded to
+ * nearest even and saturated to +-448 (all fp32, correctly rounded).
+ * BF16 copies the bits. */
+EP_API int ep_dispatch(const ep_config_t* cfg, const void* x,
+                       const int32_t* slot, int recv_dtype, void* recv,
+                       float* recv_scales, void* stream);
+
+/* Combine ([DAY2] "DeepEP是什么", and accumulation in "All-to-All通信";
+ * BF16: [NEWS] "具体性能方面").
+ *   y       device, bf16 [T*k, H] expert outputs in receive-row order,
+ *           16-byte aligned
+ *   slot    device, int32 [T, k]; pairs with slot outside [0, T*k) are
+ *           skipped
+ *   topk_w  device, fp32 [T, k]
+ *   out     device, bf16 [T, H], 16-byte aligned
+ * out[t,c] = bf16_rne(acc) where acc starts at +0 and, for j = 0..k-1 in
+ * order, acc = fma(topk_w[t,j], y[slot[t,j], c], acc) in fp32. */
+EP_API int ep_combine(const ep_config_t* cfg, const void* y,
+                      const int32_t* slot, const float* topk_w, void* out,
+                      void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* EP_H */
