@@ -9,6 +9,9 @@ top-8 experts, 32 virtual ranks by default).  Expert outputs for the combine
 are a resident synthetic buffer (the expert computation is not part of the
 path).
 
+Every buffer exists in several copies used round-robin, so that each step
+reads its inputs from HBM rather than from the 256 MB Infinity Cache.
+
 Prints one JSON line.  `value` is dispatch+combine algorithmic bytes divided
 by the summed average durations of the dispatch and combine kernels, from
 HIP events recorded on the launch stream over the timed steps.  The
@@ -16,7 +19,7 @@ HIP events recorded on the launch stream over the timed steps.  The
 times the single-threaded CPU oracle on the same batch.
 
 usage: python bench.py [--gpus 1] [--steps 20] [--warmup 5]
-                       [--config prefill] [--flush] [--no-cpu-baseline]
+                       [--config prefill] [--sets N] [--no-cpu-baseline]
 """
 from __future__ import annotations
 
@@ -36,11 +39,35 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="prefill")
-    ap.add_argument("--flush", action="store_true",
-                    help="write a 1 GiB buffer before each step so no input is cached (not timed)")
+    ap.add_argument("--sets", type=int, default=0,
+                    help="copies of all buffers used round-robin (0: enough for >= 2 GiB between reuses)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="only run a plain 1 GiB device-to-device copy (for scaling HBM counters)")
     return ap.parse_args()
+
+
+def copy_probe():
+    """A plain copy of known size: 5 x 1 GiB device-to-device copies.  Its
+    FETCH_SIZE / WRITE_SIZE readings give the factor between those counters
+    and bytes actually moved."""
+    import torch
+    n = 1 << 30
+    a = torch.ones(n, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    b.copy_(a)
+    torch.cuda.synchronize()
+    s.record()
+    for _ in range(5):
+        b.copy_(a)
+    e.record()
+    torch.cuda.synchronize()
+    t = s.elapsed_time(e) / 5 * 1e-3
+    print(json.dumps({"kind": "copy_probe", "bytes_read": n, "bytes_written": n,
+                      "us": round(t * 1e6, 1), "gbs_read_plus_write": round(2 * n / t / 1e9, 1)}), flush=True)
+    return 0
 
 
 def main():
@@ -49,6 +76,8 @@ def main():
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(--gpus %d requested)" % args.gpus, file=sys.stderr)
         return 2
+    if args.copy_probe:
+        return copy_probe()
 
     import numpy as np
     import torch
@@ -62,65 +91,78 @@ def main():
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
 
-    # resident inputs
+    # Resident inputs and outputs, in `nsets` copies used round-robin so that
+    # no step finds its data in the 256 MB Infinity Cache or the L2s: between
+    # two uses of a copy the other steps move >= 2 GiB through memory.
     lg_np, x_np, y_np = W.gen_logits(w), W.gen_x(w), W.gen_y(w)
-    logits = torch.from_numpy(lg_np).to(dev)
-    x = torch.from_numpy(x_np.view(np.int16)).view(torch.bfloat16).to(dev)
-    y = torch.from_numpy(y_np.view(np.int16)).view(torch.bfloat16).to(dev)
+    set_bytes = w.bytes_dispatch_fp8() + w.bytes_combine() + w.bytes_route()
+    nsets = args.sets or int(min(256, max(4, -(-(2 << 30) // set_bytes))))
+    logits0 = torch.from_numpy(lg_np).to(dev)
+    x0 = torch.from_numpy(x_np.view(np.int16)).view(torch.bfloat16).to(dev)
+    y0 = torch.from_numpy(y_np.view(np.int16)).view(torch.bfloat16).to(dev)
     i32 = dict(dtype=torch.int32, device=dev)
-    idx = torch.empty((w.T, w.k), **i32)
-    wt = torch.empty((w.T, w.k), dtype=torch.float32, device=dev)
-    cnt, ntok, off = torch.empty(w.E, **i32), torch.empty(w.R, **i32), torch.empty(w.E + 1, **i32)
-    slot, recv_token = torch.empty((w.T, w.k), **i32), torch.empty(w.nrows, **i32)
     ws = torch.empty(max(16, ep.layout_workspace_bytes(cfg)), dtype=torch.uint8, device=dev)
-    recv = torch.empty((w.nrows, w.H), dtype=torch.uint8, device=dev)
-    scales = torch.empty((w.nrows, w.H // 128), dtype=torch.float32, device=dev)
-    out = torch.empty((w.T, w.H), dtype=torch.bfloat16, device=dev)
-    flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev) if args.flush else None
+    sets = []
+    for i in range(nsets):
+        b = dict(
+            logits=logits0 if i == 0 else logits0.clone(),
+            x=x0 if i == 0 else x0.clone(),
+            y=y0 if i == 0 else y0.clone(),
+            idx=torch.empty((w.T, w.k), **i32),
+            wt=torch.empty((w.T, w.k), dtype=torch.float32, device=dev),
+            cnt=torch.empty(w.E, **i32), ntok=torch.empty(w.R, **i32), off=torch.empty(w.E + 1, **i32),
+            slot=torch.empty((w.T, w.k), **i32), recv_token=torch.empty(w.nrows, **i32),
+            recv=torch.empty((w.nrows, w.H), dtype=torch.uint8, device=dev),
+            scales=torch.empty((w.nrows, w.H // 128), dtype=torch.float32, device=dev),
+            out=torch.empty((w.T, w.H), dtype=torch.bfloat16, device=dev))
+        sets.append(b)
 
     stream = torch.cuda.current_stream(dev)
     sh = int(stream.cuda_stream)
     lib = L.lib()
     c = cfg.c()
     cp = ctypes.byref(c)
-    p = lambda t: t.data_ptr()  # noqa: E731
     # validate once through the checked binding, then call the C ABI directly
-    ep.route(cfg, logits, idx, wt)
-    ep.get_layout(cfg, idx, dict(cnt=cnt, ntok_rank=ntok, off=off, slot=slot, recv_token=recv_token), ws)
-    ep.dispatch(cfg, x, slot, "fp8", recv, scales)
-    ep.combine(cfg, y, slot, wt, out)
+    for b in sets:
+        ep.route(cfg, b["logits"], b["idx"], b["wt"])
+        ep.get_layout(cfg, b["idx"], dict(cnt=b["cnt"], ntok_rank=b["ntok"], off=b["off"], slot=b["slot"],
+                                          recv_token=b["recv_token"]), ws)
+        ep.dispatch(cfg, b["x"], b["slot"], "fp8", b["recv"], b["scales"])
+        ep.combine(cfg, b["y"], b["slot"], b["wt"], b["out"])
     torch.cuda.synchronize()
+    ptr = [{k: v.data_ptr() for k, v in b.items()} for b in sets]
 
     def check(rc, name):
         if rc != 0:
             raise RuntimeError("%s failed: %s" % (name, lib.ep_strerror(rc).decode()))
 
     stages = ("route", "layout", "dispatch", "combine")
+    nws = ws.numel()
 
-    def step(ev):
-        if flush is not None:
-            flush.fill_(1)
+    def step(i, ev):
+        p = ptr[i % nsets]
         ev[0].record(stream)
-        check(lib.ep_route(cp, p(logits), p(idx), p(wt), sh), "ep_route")
+        check(lib.ep_route(cp, p["logits"], p["idx"], p["wt"], sh), "ep_route")
         ev[1].record(stream)
-        check(lib.ep_get_layout(cp, p(idx), p(cnt), p(ntok), p(off), p(slot), p(recv_token), p(ws),
-                                ws.numel(), sh), "ep_get_layout")
+        check(lib.ep_get_layout(cp, p["idx"], p["cnt"], p["ntok"], p["off"], p["slot"], p["recv_token"],
+                                ws.data_ptr(), nws, sh), "ep_get_layout")
         ev[2].record(stream)
-        check(lib.ep_dispatch(cp, p(x), p(slot), L.EP_RECV_FP8_E4M3, p(recv), p(scales), sh), "ep_dispatch")
+        check(lib.ep_dispatch(cp, p["x"], p["slot"], L.EP_RECV_FP8_E4M3, p["recv"], p["scales"], sh),
+              "ep_dispatch")
         ev[3].record(stream)
-        check(lib.ep_combine(cp, p(y), p(slot), p(wt), p(out), sh), "ep_combine")
+        check(lib.ep_combine(cp, p["y"], p["slot"], p["wt"], p["out"], sh), "ep_combine")
         ev[4].record(stream)
 
     mk = lambda: [torch.cuda.Event(enable_timing=True) for _ in range(5)]  # noqa: E731
-    for _ in range(args.warmup):
-        step(mk())
+    for i in range(max(args.warmup, 0)):
+        step(i, mk())
     torch.cuda.synchronize()
 
     evs = [mk() for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for ev in evs:
-        step(ev)
+    for i, ev in enumerate(evs):
+        step(args.warmup + i, ev)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
@@ -140,13 +182,7 @@ def main():
                           algorithmic_bytes=bytes_[s], gbs=bytes_[s] / avg[s] / 1e9,
                           frac=bytes_[s] / avg[s] / 1e9 / HBM_PEAK_GBS) for s in stages}
 
-    traffic = None
-    tfile = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles", "combine_prefill_traffic.json")
-    if os.path.exists(tfile) and args.config == "prefill":
-        with open(tfile) as f:
-            tr = json.load(f)
-        if tr.get("kernel_source_sha") == _kernel_sha():
-            traffic = tr.get("traffic_bytes")
+    traffic = _recorded_traffic(args.config)
 
     comb_gbs = bytes_["combine"] / avg["combine"] / 1e9
     rec = {
@@ -165,7 +201,7 @@ def main():
         "config": {"workload": w.name, "tokens": w.T, "hidden": w.H, "experts": w.E, "groups": w.G,
                    "topk_groups": w.TG, "topk": w.k, "virtual_ranks": w.R,
                    "dispatch": "fp8_e4m3_1x128_fp32_scales", "combine": "bf16_fp32_accumulate",
-                   "flush_between_steps": bool(args.flush)},
+                   "buffer_sets": nsets},
         "frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4),
         "dispatch_combine_us": round(dc_time * 1e6, 2),
         "tokens_per_s": round(w.T / dc_time, 1),
@@ -182,6 +218,26 @@ def main():
 
     print(json.dumps(rec), flush=True)
     return 0
+
+
+def _recorded_traffic(config: str):
+    """HBM bytes per combine launch from the committed counter summary, if it
+    was taken on the current combine source (else None)."""
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles", "combine_%s_pmc.txt" % config)
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and not line.startswith(" "):
+                k, v = line.split(":", 1)
+                fields[k.strip()] = v.strip()
+    if fields.get("combine_source_sha") != _kernel_sha():
+        return None
+    try:
+        return int(fields["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
 
 
 def _kernel_sha() -> str:
