@@ -9,10 +9,12 @@
 //
 // A lane owns 8 channels: it issues up to 8 of its 16-byte row loads before
 // the first multiply-add, so that 128 bytes per lane are in flight, then
-// stores one 16-byte bf16 result.  Loads and the store are non-temporal
-// (streamed past the caches): nothing here is read twice, and on gfx950
-// this ran about 12% faster than cached stores with cold caches.  Row indices and weights are loaded once per
-// wavefront and broadcast with v_readlane.
+// stores one 16-byte bf16 result.  Row indices and weights are loaded once
+// per wavefront and broadcast with v_readlane, so row addresses are
+// wave-uniform (one buffer resource per row, in scalar registers).  Loads
+// and the store are streaming (nt): nothing is read twice.  Measured on
+// MI355X at 4096 tokens x 7168 channels, top-8: 91 us with nt loads, 99 us
+// with cached loads.
 #include "device.h"
 #include "launch.h"
 
@@ -23,73 +25,78 @@ namespace {
 // k rows are gathered in batches of B: all B loads of a batch are issued
 // before its multiply-adds, which keep the pick order j = 0, 1, ...
 template <int B>
-__global__ __launch_bounds__(1024) void combine_kernel(const uint16_t* __restrict__ y,
-                                                        const int32_t* __restrict__ slot,
-                                                        const float* __restrict__ w,
-                                                        uint16_t* __restrict__ out, int H, int k, int nrows,
-                                                        int segs) {
-    const int lane = threadIdx.x & 63;
-    const int t = blockIdx.x / segs;
-    const int seg = blockIdx.x - t * segs;
-    const int chunk = seg * blockDim.x + threadIdx.x;  // 8-channel piece of row t
+__global__ __launch_bounds__(64, 8) void combine_kernel(const uint16_t* __restrict__ y,
+                                                      const int32_t* __restrict__ slot,
+                                                      const float* __restrict__ w,
+                                                      uint16_t* __restrict__ out, int H, int k, int nrows,
+                                                      int segs, int items) {
+    const int lane = threadIdx.x;
     const int nchunks = H >> 3;
+    const uint32_t row_bytes = (uint32_t)H * 2u;
+    for (int item = blockIdx.x; item < items; item += gridDim.x) {
+        const int t = item / segs;
+        const int chunk = (item - t * segs) * 64 + lane;  // 8-channel piece of row t
 
-    int my_slot = -1;
-    float my_w = 0.0f;
-    if (lane < k) {
-        my_slot = slot[(size_t)t * k + lane];
-        my_w = w[(size_t)t * k + lane];
-    }
+        int my_slot = -1;
+        float my_w = 0.0f;
+        if (lane < k) {
+            my_slot = slot[(size_t)t * k + lane];
+            my_w = w[(size_t)t * k + lane];
+        }
 
-    if (chunk < nchunks) {
-        float acc[8];
+        if (chunk < nchunks) {
+            float acc[8];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
-        for (int j0 = 0; j0 < k; j0 += B) {
-            u32x4 v[B];
+            for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
+            for (int j0 = 0; j0 < k; j0 += B) {
+                i32x4 v[B];
 #pragma unroll
-            for (int j = 0; j < B; ++j) {
-                v[j] = u32x4{0u, 0u, 0u, 0u};
-                if (j0 + j < k) {
-                    const int r = __builtin_amdgcn_readlane(my_slot, j0 + j);
-                    if ((unsigned)r < (unsigned)nrows)
-                        v[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(y + (size_t)r * H) + chunk);
+                for (int j = 0; j < B; ++j) {
+                    v[j] = i32x4{0, 0, 0, 0};
+                    if (j0 + j < k) {
+                        const int r = __builtin_amdgcn_readlane(my_slot, j0 + j);
+                        if ((unsigned)r < (unsigned)nrows) {
+                            const auto yr = buffer_rsrc(y + (size_t)r * H, row_bytes);
+                            v[j] = __builtin_amdgcn_raw_buffer_load_b128(yr, chunk * 16, 0, kStream);
+                        }
+                    }
                 }
-            }
 #pragma unroll
-            for (int j = 0; j < B; ++j) {
-                if (j0 + j < k) {
-                    const int r = __builtin_amdgcn_readlane(my_slot, j0 + j);
-                    if ((unsigned)r < (unsigned)nrows) {
-                        const float wj = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(my_w), j0 + j));
-                        acc[0] = __builtin_fmaf(wj, bf16_lo(v[j].x), acc[0]);
-                        acc[1] = __builtin_fmaf(wj, bf16_hi(v[j].x), acc[1]);
-                        acc[2] = __builtin_fmaf(wj, bf16_lo(v[j].y), acc[2]);
-                        acc[3] = __builtin_fmaf(wj, bf16_hi(v[j].y), acc[3]);
-                        acc[4] = __builtin_fmaf(wj, bf16_lo(v[j].z), acc[4]);
-                        acc[5] = __builtin_fmaf(wj, bf16_hi(v[j].z), acc[5]);
-                        acc[6] = __builtin_fmaf(wj, bf16_lo(v[j].w), acc[6]);
-                        acc[7] = __builtin_fmaf(wj, bf16_hi(v[j].w), acc[7]);
+                for (int j = 0; j < B; ++j) {
+                    if (j0 + j < k) {
+                        const int r = __builtin_amdgcn_readlane(my_slot, j0 + j);
+                        if ((unsigned)r < (unsigned)nrows) {
+                            const float wj =
+                                __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(my_w), j0 + j));
+                            acc[0] = __builtin_fmaf(wj, bf16_lo(v[j].x), acc[0]);
+                            acc[1] = __builtin_fmaf(wj, bf16_hi(v[j].x), acc[1]);
+                            acc[2] = __builtin_fmaf(wj, bf16_lo(v[j].y), acc[2]);
+                            acc[3] = __builtin_fmaf(wj, bf16_hi(v[j].y), acc[3]);
+                            acc[4] = __builtin_fmaf(wj, bf16_lo(v[j].z), acc[4]);
+                            acc[5] = __builtin_fmaf(wj, bf16_hi(v[j].z), acc[5]);
+                            acc[6] = __builtin_fmaf(wj, bf16_lo(v[j].w), acc[6]);
+                            acc[7] = __builtin_fmaf(wj, bf16_hi(v[j].w), acc[7]);
+                        }
                     }
                 }
             }
+            i32x4 o;
+            o.x = (int)pack_bf16x2(acc[0], acc[1]);
+            o.y = (int)pack_bf16x2(acc[2], acc[3]);
+            o.z = (int)pack_bf16x2(acc[4], acc[5]);
+            o.w = (int)pack_bf16x2(acc[6], acc[7]);
+            const auto orr = buffer_rsrc(out + (size_t)t * H, row_bytes);
+            __builtin_amdgcn_raw_buffer_store_b128(o, orr, chunk * 16, 0, kStream);
         }
-        u32x4 o;
-        o.x = pack_bf16x2(acc[0], acc[1]);
-        o.y = pack_bf16x2(acc[2], acc[3]);
-        o.z = pack_bf16x2(acc[4], acc[5]);
-        o.w = pack_bf16x2(acc[6], acc[7]);
-        __builtin_nontemporal_store(o, reinterpret_cast<u32x4*>(out + (size_t)t * H) + chunk);
     }
 }
 
 template <int B>
 hipError_t launch(const Shape& s, const uint16_t* y, const int32_t* slot, const float* w, uint16_t* out,
                   hipStream_t st) {
-    const RowGeometry g = row_geometry(s.T, s.H >> 3);
-    const long blocks = (long)s.T * g.segs;
-    hipLaunchKernelGGL(combine_kernel<B>, dim3((unsigned)blocks), dim3(g.threads), 0, st, y, slot, w, out,
-                       s.H, s.k, s.T * s.k, g.segs);
+    const RowGrid g = row_grid(s.T, s.H >> 3);
+    hipLaunchKernelGGL(combine_kernel<B>, dim3(g.blocks), dim3(64), 0, st, y, slot, w, out, s.H, s.k,
+                       s.T * s.k, g.segs, g.items);
     return hipGetLastError();
 }
 

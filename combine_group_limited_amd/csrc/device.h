@@ -7,8 +7,21 @@
 namespace ep {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kWave = 64;
+
+// Cache policy bits of buffer loads and stores (gfx950): 0 = default
+// (cached), 2 = nt (streaming: the lines are not kept for reuse).
+constexpr int kCached = 0;
+constexpr int kStream = 2;
+
+// Raw buffer resource over `bytes` bytes at `base`.  Accesses at or past
+// `bytes` read zero and drop stores, so each row gets its own resource and
+// an access can never leave its row.  Word 3 selects 32-bit raw data.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }

@@ -31,26 +31,22 @@ hipError_t launch_dispatch_bf16(const Shape& s, const uint16_t* x, const int32_t
 hipError_t launch_combine(const Shape& s, const uint16_t* y, const int32_t* slot, const float* w,
                           uint16_t* out, hipStream_t stream);
 
-// Workgroup geometry of the row kernels (dispatch, combine): a token's row is
-// cut into `chunks` lane-sized pieces; a workgroup of `threads` lanes covers
-// `threads` consecutive pieces of one token, and `segs` workgroups cover a
-// row.  Large batches use one workgroup per row so that all stores of a row
-// leave from one XCD's L2; small batches use one-wave workgroups so that the
-// rows spread over every CU.
-struct RowGeometry {
-    int threads;
-    int segs;
+// Grid of the row kernels (dispatch, combine): one-wave workgroups, each
+// taking one 64-lane piece of a token's row (`segs` pieces per row) per
+// iteration; the grid is capped and the workgroups stride over the T * segs
+// pieces, so any T fits the launch limits.
+struct RowGrid {
+    int segs;   // 64-lane pieces per row
+    int items;  // T * segs
+    int blocks; // workgroups launched
 };
 
-inline RowGeometry row_geometry(int T, int chunks) {
-    const int waves_per_row = (chunks + 63) / 64;
-    RowGeometry g;
-    if ((long)T * 1 >= 2048 && waves_per_row <= 16) {
-        g.threads = waves_per_row * 64;
-    } else {
-        g.threads = 64;
-    }
-    g.segs = (chunks + g.threads - 1) / g.threads;
+inline RowGrid row_grid(int T, int lanes_per_row) {
+    constexpr int kMaxBlocks = 1 << 20;
+    RowGrid g;
+    g.segs = (lanes_per_row + 63) / 64;
+    g.items = T * g.segs;
+    g.blocks = g.items < kMaxBlocks ? g.items : kMaxBlocks;
     return g;
 }
 
