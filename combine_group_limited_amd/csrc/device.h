@@ -50,14 +50,14 @@ __device__ __forceinline__ uint32_t pack_e4m3x4(float a, float b, float c, float
 // x in [-86, 88] the scale 2^n is a normal number and the final multiply is
 // exact; beyond that the result is 0 or +inf.
 __device__ __forceinline__ float cw_expf(float x) {
-    if (__builtin_isnan(x)) return x;
-    if (x > 88.0f) return __builtin_huge_valf();
-    if (x < -86.0f) return 0.0f;
+    // branch-free: the polynomial path runs on x clamped to [-86, 88] (where
+    // it equals x) and the out-of-range results are selected afterwards
+    const float xc = __builtin_fminf(__builtin_fmaxf(x, -86.0f), 88.0f);
     const float L2E = 0x1.715476p+0f;
     const float C1 = 0x1.62ep-1f;
     const float C2 = 0x1.0bfbe8p-15f;
-    float n = __builtin_rintf(x * L2E);
-    float r = __builtin_fmaf(-n, C1, x);
+    float n = __builtin_rintf(xc * L2E);
+    float r = __builtin_fmaf(-n, C1, xc);
     r = __builtin_fmaf(-n, C2, r);
     float p = 0x1.a01a02p-13f;                 // 1/7!
     p = __builtin_fmaf(p, r, 0x1.6c16c2p-10f);  // 1/6!
@@ -67,10 +67,55 @@ __device__ __forceinline__ float cw_expf(float x) {
     p = __builtin_fmaf(p, r, 0.5f);             // 1/2!
     p = __builtin_fmaf(p, r, 1.0f);             // 1/1!
     p = __builtin_fmaf(p, r, 1.0f);             // 1/0!
-    return p * __uint_as_float((uint32_t)((int)n + 127) << 23);
+    float y = p * __uint_as_float((uint32_t)((int)n + 127) << 23);
+    y = x > 88.0f ? __builtin_huge_valf() : y;
+    y = x < -86.0f ? 0.0f : y;
+    return __builtin_isnan(x) ? x : y;
 }
 
 __device__ __forceinline__ float sigmoid(float x) { return 1.0f / (1.0f + cw_expf(-x)); }
+
+// DPP lane permutations (gfx9 encodings).  Each pairs every lane with one
+// partner inside an aligned group of 2, 4, 8 or 16 lanes; used for
+// symmetric merges, where any pairing across the two halves of the group
+// works once each half holds identical values.
+constexpr int kDppXor1 = 0xB1;        // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;        // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141; // lane i <-> 7 - i within 8
+constexpr int kDppMirror = 0x140;     // lane i <-> 15 - i within 16
+
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, CTRL, 0xF, 0xF, false);
+}
+
+// Partner value across aligned lane groups of size 2D (D = 1 .. 32, a
+// compile-time constant): lane i reads a lane of the other half of its
+// group.  D = 16 swaps the halves of each 32-lane half-wave (ds_swizzle,
+// xor mask 16); D = 32 the two half-waves.
+template <int D>
+__device__ __forceinline__ uint32_t partner_u32(uint32_t v) {
+    if constexpr (D == 1) return dpp_u32<kDppXor1>(v);
+    else if constexpr (D == 2) return dpp_u32<kDppXor2>(v);
+    else if constexpr (D == 4) return dpp_u32<kDppHalfMirror>(v);
+    else if constexpr (D == 8) return dpp_u32<kDppMirror>(v);
+    else if constexpr (D == 16) return (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, 0x401F);
+    else return (uint32_t)__shfl_xor((int)v, 32, kWave);
+}
+
+// Largest 32-bit unsigned value across a fully active wavefront, as a
+// wave-uniform value: row-wise butterfly with DPP, then the four row maxima.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+    v = max(v, dpp_u32<kDppXor1>(v));
+    v = max(v, dpp_u32<kDppXor2>(v));
+    v = max(v, dpp_u32<kDppHalfMirror>(v));
+    v = max(v, dpp_u32<kDppMirror>(v));
+    const uint32_t a = (uint32_t)__builtin_amdgcn_readlane((int)v, 0);
+    const uint32_t b = (uint32_t)__builtin_amdgcn_readlane((int)v, 16);
+    const uint32_t c = (uint32_t)__builtin_amdgcn_readlane((int)v, 32);
+    const uint32_t d = (uint32_t)__builtin_amdgcn_readlane((int)v, 48);
+    return max(max(a, b), max(c, d));
+}
 
 // Largest 64-bit value across the wavefront (every lane gets it).
 __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
