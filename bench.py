@@ -18,8 +18,14 @@ HIP events recorded on the launch stream over the timed steps.  The
 `roofline` object reports the dominant kernel (combine); `cpu_baseline`
 times the single-threaded CPU oracle on the same batch.
 
-usage: python bench.py [--gpus 1] [--steps 20] [--warmup 5]
-                       [--config prefill] [--sets N] [--no-cpu-baseline]
+Other workloads (--config), the BF16 payload (--recv-dtype bf16) and the
+low-latency path (--path ll: route + dispatch_ll + combine_ll into
+fixed-capacity receive rows, decode workload by default; `value` is then the
+dispatch+combine time in microseconds) print the same kind of line.
+
+usage: python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--config NAME]
+                       [--path normal|ll] [--recv-dtype fp8|bf16]
+                       [--capacity N] [--sets N] [--no-cpu-baseline]
 """
 from __future__ import annotations
 
@@ -90,7 +96,12 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", default="prefill")
+    ap.add_argument("--config", default=None,
+                    help="workload (default: prefill for the normal path, decode for the low-latency path)")
+    ap.add_argument("--path", choices=("normal", "ll"), default="normal",
+                    help="normal: route + layout + dispatch + combine; ll: route + dispatch_ll + combine_ll")
+    ap.add_argument("--recv-dtype", choices=("fp8", "bf16"), default="fp8", help="dispatch payload")
+    ap.add_argument("--capacity", type=int, default=0, help="low-latency rows per expert (0: T)")
     ap.add_argument("--sets", type=int, default=0,
                     help="copies of all buffers used round-robin (0: enough for >= 2 GiB between reuses)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -98,6 +109,17 @@ def parse():
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (for scaling HBM counters)")
     return ap.parse_args()
+
+
+def buffer_sets(requested: int, touched: int, allocated: int) -> int:
+    """Copies of the buffers used round-robin: enough that >= 2 GiB of
+    touched data lies between two uses of a copy (the Infinity Cache holds
+    256 MB), at least 4, at most 256, and at most 48 GiB allocated."""
+    if requested:
+        return requested
+    n = max(4, -(-(2 << 30) // max(touched, 1)))
+    n = min(n, 256, max(4, (48 << 30) // max(allocated, 1)))
+    return int(n)
 
 
 def copy_probe():
@@ -122,15 +144,48 @@ def copy_probe():
     return 0
 
 
-def main():
-    args = parse()
-    if args.gpus != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(--gpus %d requested)" % args.gpus, file=sys.stderr)
-        return 2
-    if args.copy_probe:
-        return copy_probe()
+HEADLINE_METRIC = "dispatch+combine HBM GB/s and % of peak at 4096 tok x 7168 hidden top-8"
 
+
+def timed_steps(args, nsets, launch_stages, stages):
+    """Runs `warmup` untimed and `steps` timed steps; each step calls
+    launch_stages(set_index, record) which records an event before each stage
+    and one after the last.  Returns (per-stage durations in seconds, wall
+    seconds of the timed steps)."""
+    import torch
+    hev = HipEvents()
+    sh = int(torch.cuda.current_stream().cuda_stream)
+    n = len(stages) + 1
+    warm = [hev.create(n) for _ in range(max(args.warmup, 0))]
+    for i, ev in enumerate(warm):
+        launch_stages(i % nsets, lambda q, ev=ev: hev.record(ev[q], sh))
+    torch.cuda.synchronize()
+    evs = [hev.create(n) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i, ev in enumerate(evs):
+        launch_stages((args.warmup + i) % nsets, lambda q, ev=ev: hev.record(ev[q], sh))
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    dur = {s: [hev.seconds(ev[i], ev[i + 1]) for ev in evs] for i, s in enumerate(stages)}
+    for ev in warm + evs:
+        hev.destroy(ev)
+    return dur, wall
+
+
+def kernel_table(dur, bytes_):
+    import numpy as np
+    out = {}
+    for s, v in dur.items():
+        avg = float(np.mean(v))
+        out[s] = {"avg_us": round(avg * 1e6, 4), "median_us": round(float(np.median(v)) * 1e6, 4),
+                  "algorithmic_bytes": bytes_[s], "gbs": round(bytes_[s] / avg / 1e9, 4),
+                  "frac": round(bytes_[s] / avg / 1e9 / HBM_PEAK_GBS, 4)}
+    return out
+
+
+def run_normal(args, w):
+    """route + layout + dispatch + combine on resident buffers."""
     import numpy as np
     import torch
 
@@ -138,17 +193,17 @@ def main():
     from combine_group_limited_amd import _lib as L
     import workloads as W
 
-    w = W.CONFIGS[args.config]
     cfg = ep.Config.of(w)
     dev = torch.device("cuda", 0)
-    torch.cuda.set_device(dev)
+    fp8 = args.recv_dtype == "fp8"
+    bytes_ = dict(route=w.bytes_route(), layout=w.bytes_layout(),
+                  dispatch=w.bytes_dispatch_fp8() if fp8 else w.bytes_dispatch_bf16(), combine=w.bytes_combine())
+    touched = sum(bytes_.values())
+    nsets = buffer_sets(args.sets, touched, touched)
 
     # Resident inputs and outputs, in `nsets` copies used round-robin so that
-    # no step finds its data in the 256 MB Infinity Cache or the L2s: between
-    # two uses of a copy the other steps move >= 2 GiB through memory.
+    # no step finds its data in the 256 MB Infinity Cache or the L2s.
     lg_np, x_np, y_np = W.gen_logits(w), W.gen_x(w), W.gen_y(w)
-    set_bytes = w.bytes_dispatch_fp8() + w.bytes_combine() + w.bytes_route()
-    nsets = args.sets or int(min(256, max(4, -(-(2 << 30) // set_bytes))))
     logits0 = torch.from_numpy(lg_np).to(dev)
     x0 = torch.from_numpy(x_np.view(np.int16)).view(torch.bfloat16).to(dev)
     y0 = torch.from_numpy(y_np.view(np.int16)).view(torch.bfloat16).to(dev)
@@ -156,7 +211,7 @@ def main():
     ws = torch.empty(max(16, ep.layout_workspace_bytes(cfg)), dtype=torch.uint8, device=dev)
     sets = []
     for i in range(nsets):
-        b = dict(
+        sets.append(dict(
             logits=logits0 if i == 0 else logits0.clone(),
             x=x0 if i == 0 else x0.clone(),
             y=y0 if i == 0 else y0.clone(),
@@ -164,84 +219,56 @@ def main():
             wt=torch.empty((w.T, w.k), dtype=torch.float32, device=dev),
             cnt=torch.empty(w.E, **i32), ntok=torch.empty(w.R, **i32), off=torch.empty(w.E + 1, **i32),
             slot=torch.empty((w.T, w.k), **i32), recv_token=torch.empty(w.nrows, **i32),
-            recv=torch.empty((w.nrows, w.H), dtype=torch.uint8, device=dev),
-            scales=torch.empty((w.nrows, w.H // 128), dtype=torch.float32, device=dev),
-            out=torch.empty((w.T, w.H), dtype=torch.bfloat16, device=dev))
-        sets.append(b)
+            recv=torch.empty((w.nrows, w.H), dtype=torch.uint8 if fp8 else torch.bfloat16, device=dev),
+            scales=torch.empty((w.nrows, w.H // 128), dtype=torch.float32, device=dev) if fp8 else None,
+            out=torch.empty((w.T, w.H), dtype=torch.bfloat16, device=dev)))
 
-    stream = torch.cuda.current_stream(dev)
-    sh = int(stream.cuda_stream)
-    lib = L.lib()
-    c = cfg.c()
-    cp = ctypes.byref(c)
     # validate once through the checked binding, then call the C ABI directly
     for b in sets:
         ep.route(cfg, b["logits"], b["idx"], b["wt"])
         ep.get_layout(cfg, b["idx"], dict(cnt=b["cnt"], ntok_rank=b["ntok"], off=b["off"], slot=b["slot"],
                                           recv_token=b["recv_token"]), ws)
-        ep.dispatch(cfg, b["x"], b["slot"], "fp8", b["recv"], b["scales"])
+        ep.dispatch(cfg, b["x"], b["slot"], args.recv_dtype, b["recv"], b["scales"])
         ep.combine(cfg, b["y"], b["slot"], b["wt"], b["out"])
     torch.cuda.synchronize()
-    ptr = [{k: v.data_ptr() for k, v in b.items()} for b in sets]
+    ptr = [{k: (v.data_ptr() if v is not None else None) for k, v in b.items()} for b in sets]
+    lib = L.lib()
+    c = cfg.c()
+    cp = ctypes.byref(c)
+    sh = int(torch.cuda.current_stream().cuda_stream)
+    code = L.EP_RECV_FP8_E4M3 if fp8 else L.EP_RECV_BF16
+    nws = ws.numel()
 
     def check(rc, name):
         if rc != 0:
             raise RuntimeError("%s failed: %s" % (name, lib.ep_strerror(rc).decode()))
 
-    stages = ("route", "layout", "dispatch", "combine")
-    nws = ws.numel()
-    hev = HipEvents()
-
-    def step(i, ev):
-        p = ptr[i % nsets]
-        hev.record(ev[0], sh)
+    def launch(i, rec):
+        p = ptr[i]
+        rec(0)
         check(lib.ep_route(cp, p["logits"], p["idx"], p["wt"], sh), "ep_route")
-        hev.record(ev[1], sh)
+        rec(1)
         check(lib.ep_get_layout(cp, p["idx"], p["cnt"], p["ntok"], p["off"], p["slot"], p["recv_token"],
                                 ws.data_ptr(), nws, sh), "ep_get_layout")
-        hev.record(ev[2], sh)
-        check(lib.ep_dispatch(cp, p["x"], p["slot"], L.EP_RECV_FP8_E4M3, p["recv"], p["scales"], sh),
-              "ep_dispatch")
-        hev.record(ev[3], sh)
+        rec(2)
+        check(lib.ep_dispatch(cp, p["x"], p["slot"], code, p["recv"], p["scales"], sh), "ep_dispatch")
+        rec(3)
         check(lib.ep_combine(cp, p["y"], p["slot"], p["wt"], p["out"], sh), "ep_combine")
-        hev.record(ev[4], sh)
+        rec(4)
 
-    warm = [hev.create(5) for _ in range(max(args.warmup, 0))]
-    for i, ev in enumerate(warm):
-        step(i, ev)
-    torch.cuda.synchronize()
-
-    evs = [hev.create(5) for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i, ev in enumerate(evs):
-        step(args.warmup + i, ev)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-
-    dur = {s: [] for s in stages}
-    for ev in evs:
-        for i, s in enumerate(stages):
-            dur[s].append(hev.seconds(ev[i], ev[i + 1]))
-    for ev in warm + evs:
-        hev.destroy(ev)
-    avg = {s: float(np.mean(v)) for s, v in dur.items()}
-    med = {s: float(np.median(v)) for s, v in dur.items()}
-
-    bytes_ = dict(route=w.bytes_route(), layout=w.bytes_layout(), dispatch=w.bytes_dispatch_fp8(),
-                  combine=w.bytes_combine())
+    stages = ("route", "layout", "dispatch", "combine")
+    dur, wall = timed_steps(args, nsets, launch, stages)
+    kt = kernel_table(dur, bytes_)
+    avg = {s: kt[s]["avg_us"] * 1e-6 for s in stages}
     dc_bytes = bytes_["dispatch"] + bytes_["combine"]
     dc_time = avg["dispatch"] + avg["combine"]
     value = dc_bytes / dc_time / 1e9
-    per_kernel = {s: dict(avg_us=avg[s] * 1e6, median_us=med[s] * 1e6,
-                          algorithmic_bytes=bytes_[s], gbs=bytes_[s] / avg[s] / 1e9,
-                          frac=bytes_[s] / avg[s] / 1e9 / HBM_PEAK_GBS) for s in stages}
-
-    traffic = _recorded_traffic(args.config)
-
+    headline = w.name == "prefill" and fp8
     comb_gbs = bytes_["combine"] / avg["combine"] / 1e9
     rec = {
-        "metric": "dispatch+combine HBM GB/s and % of peak at 4096 tok x 7168 hidden top-8",
+        "metric": HEADLINE_METRIC if headline else
+        "dispatch+combine HBM GB/s and %% of peak at %d tok x %d hidden top-%d (%s dispatch)" % (
+            w.T, w.H, w.k, args.recv_dtype.upper()),
         "value": round(value, 1),
         "unit": "GB/s",
         "n_gpus": 1,
@@ -253,41 +280,162 @@ def main():
         "vs_baseline": None,
         "dtype": "fp32",
         "data": "synthetic",
-        "config": {"workload": w.name, "tokens": w.T, "hidden": w.H, "experts": w.E, "groups": w.G,
-                   "topk_groups": w.TG, "topk": w.k, "virtual_ranks": w.R,
-                   "dispatch": "fp8_e4m3_1x128_fp32_scales", "combine": "bf16_fp32_accumulate",
-                   "buffer_sets": nsets},
+        "config": {"workload": w.name, "path": "normal", "tokens": w.T, "hidden": w.H, "experts": w.E,
+                   "groups": w.G, "topk_groups": w.TG, "topk": w.k, "virtual_ranks": w.R,
+                   "dispatch": "fp8_e4m3_1x128_fp32_scales" if fp8 else "bf16",
+                   "combine": "bf16_fp32_accumulate", "buffer_sets": nsets},
         "frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4),
         "dispatch_combine_us": round(dc_time * 1e6, 2),
         "tokens_per_s": round(w.T / dc_time, 1),
         "step_tokens_per_s": round(w.T / (wall / args.steps), 1),
         "roofline": {"kernel": "combine", "bound": "hbm", "achieved": round(comb_gbs, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(comb_gbs / HBM_PEAK_GBS, 4),
-                     "traffic": traffic},
-        "kernels": {s: {k2: (round(v, 4) if isinstance(v, float) else v) for k2, v in d.items()}
-                    for s, d in per_kernel.items()},
+                     "traffic": _recorded_traffic("combine", w.name)},
+        "kernels": kt,
     }
-
-    if not args.no_cpu_baseline:
+    dkey = "dispatch_fp8" if fp8 else "dispatch_bf16"
+    rec["kernels"]["dispatch"]["traffic"] = _recorded_traffic(dkey, w.name)
+    if not args.no_cpu_baseline and fp8:
         rec["cpu_baseline"] = cpu_baseline(w, lg_np, x_np, y_np, args.cpu_seconds)
+    return rec
 
+
+def run_ll(args, w):
+    """route + dispatch_ll + combine_ll (fixed-capacity receive rows) on
+    resident buffers."""
+    import numpy as np
+    import torch
+
+    import combine_group_limited_amd as ep
+    from combine_group_limited_amd import _lib as L
+    import workloads as W
+
+    cfg = ep.Config.of(w)
+    dev = torch.device("cuda", 0)
+    fp8 = args.recv_dtype == "fp8"
+    cap = args.capacity or w.T
+    nrows = w.E * cap
+    bytes_ = dict(route=w.bytes_route(),
+                  dispatch_ll=(w.bytes_dispatch_fp8() if fp8 else w.bytes_dispatch_bf16()),
+                  combine_ll=w.bytes_combine())
+    touched = sum(bytes_.values())
+    allocated = nrows * w.H * (1 if fp8 else 2) + nrows * w.H * 2 + touched
+    nsets = buffer_sets(args.sets, touched, allocated)
+
+    lg_np, x_np = W.gen_logits(w), W.gen_x(w)
+    logits0 = torch.from_numpy(lg_np).to(dev)
+    x0 = torch.from_numpy(x_np.view(np.int16)).view(torch.bfloat16).to(dev)
+    y0 = torch.randn((nrows, w.H), device=dev).to(torch.bfloat16)   # expert outputs, any values
+    i32 = dict(dtype=torch.int32, device=dev)
+    sets = []
+    for i in range(nsets):
+        sets.append(dict(
+            logits=logits0 if i == 0 else logits0.clone(),
+            x=x0 if i == 0 else x0.clone(),
+            y=y0 if i == 0 else y0.clone(),
+            idx=torch.empty((w.T, w.k), **i32),
+            wt=torch.empty((w.T, w.k), dtype=torch.float32, device=dev),
+            count=torch.empty(w.E, **i32), src=torch.empty(nrows, **i32), slot=torch.empty((w.T, w.k), **i32),
+            recv=torch.empty((nrows, w.H), dtype=torch.uint8 if fp8 else torch.bfloat16, device=dev),
+            scales=torch.empty((nrows, w.H // 128), dtype=torch.float32, device=dev) if fp8 else None,
+            out=torch.empty((w.T, w.H), dtype=torch.bfloat16, device=dev)))
+    for b in sets:
+        ep.route(cfg, b["logits"], b["idx"], b["wt"])
+        ep.dispatch_ll(cfg, b["x"], b["idx"], cap, args.recv_dtype, b["recv"], b["scales"], b["count"], b["src"],
+                       b["slot"])
+        ep.combine_ll(cfg, cap, b["y"], b["slot"], b["wt"], b["out"])
+    torch.cuda.synchronize()
+    ptr = [{k: (v.data_ptr() if v is not None else None) for k, v in b.items()} for b in sets]
+    lib = L.lib()
+    c = cfg.c()
+    cp = ctypes.byref(c)
+    sh = int(torch.cuda.current_stream().cuda_stream)
+    code = L.EP_RECV_FP8_E4M3 if fp8 else L.EP_RECV_BF16
+
+    def check(rc, name):
+        if rc != 0:
+            raise RuntimeError("%s failed: %s" % (name, lib.ep_strerror(rc).decode()))
+
+    def launch(i, rec):
+        p = ptr[i]
+        rec(0)
+        check(lib.ep_route(cp, p["logits"], p["idx"], p["wt"], sh), "ep_route")
+        rec(1)
+        check(lib.ep_dispatch_ll(cp, p["x"], p["idx"], cap, code, p["recv"], p["scales"], p["count"], p["src"],
+                                 p["slot"], sh), "ep_dispatch_ll")
+        rec(2)
+        check(lib.ep_combine_ll(cp, cap, p["y"], p["slot"], p["wt"], p["out"], sh), "ep_combine_ll")
+        rec(3)
+
+    stages = ("route", "dispatch_ll", "combine_ll")
+    dur, wall = timed_steps(args, nsets, launch, stages)
+    kt = kernel_table(dur, bytes_)
+    avg = {s: kt[s]["avg_us"] * 1e-6 for s in stages}
+    dc_time = avg["dispatch_ll"] + avg["combine_ll"]
+    dc_bytes = bytes_["dispatch_ll"] + bytes_["combine_ll"]
+    comb_gbs = bytes_["combine_ll"] / avg["combine_ll"] / 1e9
+    rec = {
+        "metric": "low-latency dispatch+combine time at %d tok x %d hidden top-%d (%s dispatch)" % (
+            w.T, w.H, w.k, args.recv_dtype.upper()),
+        "value": round(dc_time * 1e6, 2),
+        "unit": "us",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall / args.steps * 1e3, 4),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "path": "low_latency", "tokens": w.T, "hidden": w.H, "experts": w.E,
+                   "groups": w.G, "topk_groups": w.TG, "topk": w.k, "capacity": cap,
+                   "dispatch": "fp8_e4m3_1x128_fp32_scales" if fp8 else "bf16",
+                   "combine": "bf16_fp32_accumulate", "buffer_sets": nsets},
+        "dispatch_combine_gbs": round(dc_bytes / dc_time / 1e9, 1),
+        "step_us": round(sum(avg.values()) * 1e6, 2),
+        "roofline": {"kernel": "combine_ll", "bound": "hbm", "achieved": round(comb_gbs, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(comb_gbs / HBM_PEAK_GBS, 4),
+                     "traffic": None},
+        "kernels": kt,
+    }
+    return rec
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(--gpus %d requested)" % args.gpus, file=sys.stderr)
+        return 2
+    if args.copy_probe:
+        return copy_probe()
+
+    import torch
+    import workloads as W
+
+    name = args.config or ("decode" if args.path == "ll" else "prefill")
+    w = W.CONFIGS[name]
+    torch.cuda.set_device(0)
+    rec = run_ll(args, w) if args.path == "ll" else run_normal(args, w)
     print(json.dumps(rec), flush=True)
     return 0
 
 
-def _recorded_traffic(config: str):
-    """HBM bytes per combine launch from the committed counter summary, if it
-    was taken on the current combine source (else None)."""
-    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles", "combine_%s_pmc.txt" % config)
+def _recorded_traffic(kernel: str, config: str):
+    """HBM bytes per launch of `kernel` from the committed counter summary
+    for `config`, if it was taken on the kernel's current source (else
+    None)."""
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles", "%s_%s_pmc.txt" % (kernel, config))
     if not os.path.exists(path):
         return None
     fields = {}
     with open(path) as f:
         for line in f:
-            if ":" in line and not line.startswith(" "):
+            if ":" in line and not line.startswith(("#", " ")):
                 k, v = line.split(":", 1)
                 fields[k.strip()] = v.strip()
-    if fields.get("combine_source_sha") != _kernel_sha():
+    if fields.get("%s_source_sha" % kernel) != kernel_sha(kernel):
         return None
     try:
         return int(fields["traffic_bytes_per_launch"])
@@ -295,11 +443,19 @@ def _recorded_traffic(config: str):
         return None
 
 
-def _kernel_sha() -> str:
+# sources each measured kernel is built from (for matching counter summaries)
+KERNEL_SOURCES = {
+    "combine": ("combine.hip", "device.h", "launch.h"),
+    "dispatch_fp8": ("dispatch.hip", "rows.h", "device.h", "launch.h"),
+    "dispatch_bf16": ("dispatch.hip", "rows.h", "device.h", "launch.h"),
+}
+
+
+def kernel_sha(kernel: str) -> str:
     import hashlib
     root = os.path.dirname(os.path.abspath(__file__))
     h = hashlib.sha256()
-    for f in ("combine.hip", "device.h", "launch.h"):
+    for f in KERNEL_SOURCES[kernel]:
         with open(os.path.join(root, "combine_group_limited_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -308,7 +464,7 @@ def _kernel_sha() -> str:
 def cpu_baseline(w, lg, x, y, seconds: float):
     """The CPU oracle (plain single-threaded C) on the same batch: route and
     layout once, then FP8 dispatch + combine passes over the whole batch,
-    repeated until `seconds` of CPU time have elapsed (at most 8 passes)."""
+    repeated until `seconds` of CPU time have elapsed (at most 64 passes)."""
     import numpy as np
 
     import oracle

@@ -8,7 +8,9 @@ from .api import (  # noqa: F401
     Config,
     EpError,
     combine,
+    combine_ll,
     dispatch,
+    dispatch_ll,
     get_layout,
     layout_workspace_bytes,
     route,

@@ -38,6 +38,8 @@ EXPORTS = (
     "ep_get_layout",
     "ep_dispatch",
     "ep_combine",
+    "ep_dispatch_ll",
+    "ep_combine_ll",
 )
 
 
@@ -88,5 +90,10 @@ def lib() -> ctypes.CDLL:
         L.ep_dispatch.restype = I
         L.ep_combine.argtypes = [C, P, P, P, P, P]
         L.ep_combine.restype = I
+        I32 = ctypes.c_int32
+        L.ep_dispatch_ll.argtypes = [C, P, P, I32, I, P, P, P, P, P, P]
+        L.ep_dispatch_ll.restype = I
+        L.ep_combine_ll.argtypes = [C, I32, P, P, P, P, P]
+        L.ep_combine_ll.restype = I
         _lib = L
         return _lib

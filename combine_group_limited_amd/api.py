@@ -186,3 +186,67 @@ def combine(cfg: Config, y: torch.Tensor, slot: torch.Tensor, topk_w: torch.Tens
     _check(L.lib().ep_combine(ctypes.byref(c), _ptr(y), _ptr(slot), _ptr(topk_w), _ptr(out),
                               _stream(stream, dev)), "ep_combine")
     return out
+
+
+def dispatch_ll(cfg: Config, x: torch.Tensor, topk_idx: torch.Tensor, capacity: int, recv_dtype: str = "fp8",
+                recv=None, recv_scales=None, recv_count=None, recv_src=None, slot=None, stream=None) -> dict:
+    """Low-latency dispatch into fixed-capacity per-expert receive rows
+    (expert e owns rows [e*capacity, (e+1)*capacity)).  Returns a dict with
+    recv ([E*capacity, H] uint8 E4M3 codes or bf16), scales (fp32
+    [E*capacity, H/128] or None), count (int32 [E]), src (int32
+    [E*capacity]) and slot (int32 [T, k]).  Rows no pair takes, and their
+    src entries, are left as they were."""
+    dev = x.device
+    _want(x, "x", (cfg.T, cfg.H), torch.bfloat16, None)
+    _want(topk_idx, "topk_idx", (cfg.T, cfg.k), torch.int32, dev)
+    nrows = cfg.E * capacity
+    i32 = dict(dtype=torch.int32, device=dev)
+    if recv_dtype == "fp8":
+        if recv is None:
+            recv = torch.empty((nrows, cfg.H), dtype=torch.uint8, device=dev)
+        if recv_scales is None:
+            recv_scales = torch.empty((nrows, cfg.H // 128), dtype=torch.float32, device=dev)
+        recv_u8 = recv.view(torch.uint8) if recv.dtype == torch.float8_e4m3fn else recv
+        _want(recv_u8, "recv", (nrows, cfg.H), torch.uint8, dev)
+        _want(recv_scales, "recv_scales", (nrows, cfg.H // 128), torch.float32, dev)
+        code = L.EP_RECV_FP8_E4M3
+    elif recv_dtype == "bf16":
+        if recv is None:
+            recv = torch.empty((nrows, cfg.H), dtype=torch.bfloat16, device=dev)
+        _want(recv, "recv", (nrows, cfg.H), torch.bfloat16, dev)
+        if recv_scales is not None:
+            raise ValueError("recv_scales must be None for bf16 dispatch")
+        code = L.EP_RECV_BF16
+    else:
+        raise ValueError("recv_dtype must be 'fp8' or 'bf16'")
+    if recv_count is None:
+        recv_count = torch.empty(cfg.E, **i32)
+    if recv_src is None:
+        recv_src = torch.empty(nrows, **i32)
+    if slot is None:
+        slot = torch.empty((cfg.T, cfg.k), **i32)
+    _want(recv_count, "recv_count", (cfg.E,), torch.int32, dev)
+    _want(recv_src, "recv_src", (nrows,), torch.int32, dev)
+    _want(slot, "slot", (cfg.T, cfg.k), torch.int32, dev)
+    c = cfg.c()
+    _check(L.lib().ep_dispatch_ll(ctypes.byref(c), _ptr(x), _ptr(topk_idx), capacity, code, _ptr(recv),
+                                  _ptr(recv_scales), _ptr(recv_count), _ptr(recv_src), _ptr(slot),
+                                  _stream(stream, dev)), "ep_dispatch_ll")
+    return dict(recv=recv, scales=recv_scales, count=recv_count, src=recv_src, slot=slot)
+
+
+def combine_ll(cfg: Config, capacity: int, y: torch.Tensor, slot: torch.Tensor, topk_w: torch.Tensor, out=None,
+               stream=None):
+    """Weighted combine of bf16 expert outputs in ep_dispatch_ll's receive
+    rows, y [E*capacity, H] -> bf16 [T, H]."""
+    dev = y.device
+    _want(y, "y", (cfg.E * capacity, cfg.H), torch.bfloat16, None)
+    _want(slot, "slot", (cfg.T, cfg.k), torch.int32, dev)
+    _want(topk_w, "topk_w", (cfg.T, cfg.k), torch.float32, dev)
+    if out is None:
+        out = torch.empty((cfg.T, cfg.H), dtype=torch.bfloat16, device=dev)
+    _want(out, "out", (cfg.T, cfg.H), torch.bfloat16, dev)
+    c = cfg.c()
+    _check(L.lib().ep_combine_ll(ctypes.byref(c), capacity, _ptr(y), _ptr(slot), _ptr(topk_w), _ptr(out),
+                                 _stream(stream, dev)), "ep_combine_ll")
+    return out

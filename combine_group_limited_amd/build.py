@@ -17,8 +17,8 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(PKG, "_build")
 LIB_PATH = os.path.join(PKG, "libep.so")
 
-SOURCES = ["api.hip", "gate.hip", "layout.hip", "dispatch.hip", "combine.hip"]
-HEADERS = ["device.h", "launch.h"]
+SOURCES = ["api.hip", "gate.hip", "layout.hip", "dispatch.hip", "combine.hip", "ll.hip"]
+HEADERS = ["device.h", "launch.h", "rows.h"]
 
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
 

@@ -46,6 +46,14 @@ int validate(const ep_config_t* c) {
     return EP_OK;
 }
 
+// the configuration plus the low-latency receive capacity (rows per expert)
+int validate_ll(const ep_config_t* c, int32_t capacity) {
+    const int rc = validate(c);
+    if (rc) return rc;
+    if (capacity < 1 || (long)c->num_experts * capacity >= (1L << 31)) return EP_ERR_INVALID_ARG;
+    return EP_OK;
+}
+
 ep::Shape shape_of(const ep_config_t* c) {
     return ep::Shape{c->num_tokens, c->hidden,    c->num_experts, c->num_groups,
                      c->topk_groups, c->topk, c->num_ranks,   effective_topm(c)};
@@ -138,7 +146,40 @@ EP_API int ep_combine(const ep_config_t* cfg, const void* y, const int32_t* slot
     if (cfg->num_tokens > 0 && (!y || !slot || !topk_w || !out)) return EP_ERR_INVALID_ARG;
     if (!aligned(y, 16) || !aligned(out, 16) || !aligned(slot, 4) || !aligned(topk_w, 4))
         return EP_ERR_ALIGNMENT;
-    return hip_status(ep::launch_combine(shape_of(cfg), static_cast<const uint16_t*>(y), slot, topk_w,
+    return hip_status(ep::launch_combine(shape_of(cfg), cfg->num_tokens * cfg->topk, static_cast<const uint16_t*>(y),
+                                         slot, topk_w, static_cast<uint16_t*>(out),
+                                         static_cast<hipStream_t>(stream)));
+}
+
+EP_API int ep_dispatch_ll(const ep_config_t* cfg, const void* x, const int32_t* topk_idx, int32_t capacity,
+                          int recv_dtype, void* recv, float* recv_scales, int32_t* recv_count, int32_t* recv_src,
+                          int32_t* slot, void* stream) {
+    int rc = validate_ll(cfg, capacity);
+    if (rc) return rc;
+    if ((long)cfg->num_tokens * cfg->topk > ep::kMaxPairsLL) return EP_ERR_UNSUPPORTED;
+    if (recv_dtype != EP_RECV_FP8_E4M3 && recv_dtype != EP_RECV_BF16) return EP_ERR_INVALID_ARG;
+    const bool fp8 = recv_dtype == EP_RECV_FP8_E4M3;
+    if (!recv_count) return EP_ERR_INVALID_ARG;
+    if (cfg->num_tokens > 0 && (!x || !topk_idx || !recv || !recv_src || !slot || (fp8 && !recv_scales)))
+        return EP_ERR_INVALID_ARG;
+    if (!fp8 && recv_scales) return EP_ERR_INVALID_ARG;
+    if (!aligned(x, 16) || !aligned(recv, 16) || !aligned(topk_idx, 4) || !aligned(recv_scales, 4) ||
+        !aligned(recv_count, 4) || !aligned(recv_src, 4) || !aligned(slot, 4))
+        return EP_ERR_ALIGNMENT;
+    return hip_status(ep::launch_dispatch_ll(shape_of(cfg), capacity, fp8, static_cast<const uint16_t*>(x), topk_idx,
+                                             recv, recv_scales, recv_count, recv_src, slot,
+                                             static_cast<hipStream_t>(stream)));
+}
+
+EP_API int ep_combine_ll(const ep_config_t* cfg, int32_t capacity, const void* y, const int32_t* slot,
+                         const float* topk_w, void* out, void* stream) {
+    int rc = validate_ll(cfg, capacity);
+    if (rc) return rc;
+    if (cfg->num_tokens > 0 && (!y || !slot || !topk_w || !out)) return EP_ERR_INVALID_ARG;
+    if (!aligned(y, 16) || !aligned(out, 16) || !aligned(slot, 4) || !aligned(topk_w, 4))
+        return EP_ERR_ALIGNMENT;
+    return hip_status(ep::launch_combine(shape_of(cfg), cfg->num_experts * capacity,
+                                         static_cast<const uint16_t*>(y), slot, topk_w,
                                          static_cast<uint16_t*>(out), static_cast<hipStream_t>(stream)));
 }
 

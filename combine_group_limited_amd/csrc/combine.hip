@@ -92,21 +92,21 @@ __global__ __launch_bounds__(64, 8) void combine_kernel(const uint16_t* __restri
 }
 
 template <int B>
-hipError_t launch(const Shape& s, const uint16_t* y, const int32_t* slot, const float* w, uint16_t* out,
-                  hipStream_t st) {
+hipError_t launch(const Shape& s, int nrows, const uint16_t* y, const int32_t* slot, const float* w,
+                  uint16_t* out, hipStream_t st) {
     const RowGrid g = row_grid(s.T, s.H >> 3);
-    hipLaunchKernelGGL(combine_kernel<B>, dim3(g.blocks), dim3(64), 0, st, y, slot, w, out, s.H, s.k,
-                       s.T * s.k, g.segs, g.items);
+    hipLaunchKernelGGL(combine_kernel<B>, dim3(g.blocks), dim3(64), 0, st, y, slot, w, out, s.H, s.k, nrows,
+                       g.segs, g.items);
     return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_combine(const Shape& s, const uint16_t* y, const int32_t* slot, const float* w,
+hipError_t launch_combine(const Shape& s, int nrows, const uint16_t* y, const int32_t* slot, const float* w,
                           uint16_t* out, hipStream_t stream) {
     if (s.T == 0) return hipSuccess;
-    if (s.k <= 4) return launch<4>(s, y, slot, w, out, stream);
-    return launch<8>(s, y, slot, w, out, stream);
+    if (s.k <= 4) return launch<4>(s, nrows, y, slot, w, out, stream);
+    return launch<8>(s, nrows, y, slot, w, out, stream);
 }
 
 }  // namespace ep

@@ -8,31 +8,28 @@
 // amax = max |x|, a = max(amax, 1e-4), inv = 448 / a, scale = a / 448,
 // code = e4m3_rne(x * inv).
 //
-// FP8 kernel: a lane owns 16 consecutive channels (two 16-byte loads of
-// bf16, one 16-byte store of codes per receive row), so a 128-channel block
-// is 8 adjacent lanes and its amax is a 3-step butterfly.  The row is read
-// from HBM once and written k times.  Receive-row indices are loaded once per
-// wavefront and broadcast with v_readlane, so each row's address is
-// wave-uniform and lives in scalar registers (one buffer resource per row).
+// One-wave workgroups stride over the (token, 64-lane piece of its row)
+// items; a lane's piece is read once and written to the token's k receive
+// rows (rows.h: 16 channels per lane for FP8, 8 for BF16).  Receive-row
+// indices are loaded once per wavefront and broadcast with v_readlane.
 //
 // Cache policy, measured on MI355X at 4096 tokens x 7168 channels, top-8:
 // streaming (nt) stores of the receive rows, default-cached loads of x
 // (49.5 us; nt loads 62 us, cached stores 65 us).
-#include "device.h"
 #include "launch.h"
+#include "rows.h"
 
 namespace ep {
 
 namespace {
 
 __global__ __launch_bounds__(64, 8) void dispatch_fp8_kernel(const uint16_t* __restrict__ x,
-                                                           const int32_t* __restrict__ slot,
-                                                           uint8_t* __restrict__ recv,
-                                                           float* __restrict__ recv_sc, int H, int k,
-                                                           int nrows, int segs, int items) {
+                                                             const int32_t* __restrict__ slot,
+                                                             uint8_t* __restrict__ recv,
+                                                             float* __restrict__ recv_sc, int H, int k,
+                                                             int nrows, int segs, int items) {
     const int lane = threadIdx.x;
     const int nchunks = H >> 4;
-    const int nblk = H >> 7;
     for (int item = blockIdx.x; item < items; item += gridDim.x) {
         const int t = item / segs;
         const int chunk = (item - t * segs) * 64 + lane;  // 16-channel piece of row t
@@ -42,49 +39,14 @@ __global__ __launch_bounds__(64, 8) void dispatch_fp8_kernel(const uint16_t* __r
         if (lane < k) my_slot = slot[(size_t)t * k + lane];
 
         // whole 8-lane groups fall outside the row together (H % 128 == 0)
-        if (chunk < nchunks) {
-            const auto xr = buffer_rsrc(x + (size_t)t * H, (uint32_t)H * 2u);
-            const i32x4 a = __builtin_amdgcn_raw_buffer_load_b128(xr, chunk * 32, 0, kCached);
-            const i32x4 b = __builtin_amdgcn_raw_buffer_load_b128(xr, chunk * 32 + 16, 0, kCached);
-            float f[16];
-            f[0] = bf16_lo(a.x);  f[1] = bf16_hi(a.x);  f[2] = bf16_lo(a.y);  f[3] = bf16_hi(a.y);
-            f[4] = bf16_lo(a.z);  f[5] = bf16_hi(a.z);  f[6] = bf16_lo(a.w);  f[7] = bf16_hi(a.w);
-            f[8] = bf16_lo(b.x);  f[9] = bf16_hi(b.x);  f[10] = bf16_lo(b.y); f[11] = bf16_hi(b.y);
-            f[12] = bf16_lo(b.z); f[13] = bf16_hi(b.z); f[14] = bf16_lo(b.w); f[15] = bf16_hi(b.w);
-
-            float amax = 0.0f;
-#pragma unroll
-            for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(f[i]));
-            amax = fmaxf(amax, __shfl_xor(amax, 1, kWave));
-            amax = fmaxf(amax, __shfl_xor(amax, 2, kWave));
-            amax = fmaxf(amax, __shfl_xor(amax, 4, kWave));
-            const float ac = fmaxf(amax, 1e-4f);
-            const float inv = 448.0f / ac;
-            const float sc = ac / 448.0f;
-
-            i32x4 q;
-            q.x = (int)pack_e4m3x4(f[0] * inv, f[1] * inv, f[2] * inv, f[3] * inv);
-            q.y = (int)pack_e4m3x4(f[4] * inv, f[5] * inv, f[6] * inv, f[7] * inv);
-            q.z = (int)pack_e4m3x4(f[8] * inv, f[9] * inv, f[10] * inv, f[11] * inv);
-            q.w = (int)pack_e4m3x4(f[12] * inv, f[13] * inv, f[14] * inv, f[15] * inv);
-
-            for (int j = 0; j < k; ++j) {
-                const int r = __builtin_amdgcn_readlane(my_slot, j);
-                if ((unsigned)r < (unsigned)nrows) {
-                    const auto rr = buffer_rsrc(recv + (size_t)r * H, (uint32_t)H);
-                    __builtin_amdgcn_raw_buffer_store_b128(q, rr, chunk * 16, 0, kStream);
-                    if ((lane & 7) == 0) recv_sc[(size_t)r * nblk + (chunk >> 3)] = sc;
-                }
-            }
-        }
+        if (chunk < nchunks) fp8_piece(x + (size_t)t * H, chunk, H, k, my_slot, nrows, recv, recv_sc);
     }
 }
 
-// BF16: a lane owns 8 channels (one 16-byte load, one 16-byte store per row).
 __global__ __launch_bounds__(64, 8) void dispatch_bf16_kernel(const uint16_t* __restrict__ x,
-                                                            const int32_t* __restrict__ slot,
-                                                            uint16_t* __restrict__ recv, int H, int k,
-                                                            int nrows, int segs, int items) {
+                                                              const int32_t* __restrict__ slot,
+                                                              uint16_t* __restrict__ recv, int H, int k,
+                                                              int nrows, int segs, int items) {
     const int lane = threadIdx.x;
     const int nchunks = H >> 3;
     for (int item = blockIdx.x; item < items; item += gridDim.x) {
@@ -94,17 +56,7 @@ __global__ __launch_bounds__(64, 8) void dispatch_bf16_kernel(const uint16_t* __
         int my_slot = -1;
         if (lane < k) my_slot = slot[(size_t)t * k + lane];
 
-        if (chunk < nchunks) {
-            const auto xr = buffer_rsrc(x + (size_t)t * H, (uint32_t)H * 2u);
-            const i32x4 v = __builtin_amdgcn_raw_buffer_load_b128(xr, chunk * 16, 0, kCached);
-            for (int j = 0; j < k; ++j) {
-                const int r = __builtin_amdgcn_readlane(my_slot, j);
-                if ((unsigned)r < (unsigned)nrows) {
-                    const auto rr = buffer_rsrc(recv + (size_t)r * H, (uint32_t)H * 2u);
-                    __builtin_amdgcn_raw_buffer_store_b128(v, rr, chunk * 16, 0, kStream);
-                }
-            }
-        }
+        if (chunk < nchunks) bf16_piece(x + (size_t)t * H, chunk, H, k, my_slot, nrows, recv);
     }
 }
 

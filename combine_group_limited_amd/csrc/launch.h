@@ -28,8 +28,19 @@ hipError_t launch_dispatch_fp8(const Shape& s, const uint16_t* x, const int32_t*
 hipError_t launch_dispatch_bf16(const Shape& s, const uint16_t* x, const int32_t* slot, uint16_t* recv,
                                 hipStream_t stream);
 
-hipError_t launch_combine(const Shape& s, const uint16_t* y, const int32_t* slot, const float* w,
+// combine over y of `nrows` rows (T * k for the normal layout, E * cap for
+// the low-latency one); slots outside [0, nrows) are skipped
+hipError_t launch_combine(const Shape& s, int nrows, const uint16_t* y, const int32_t* slot, const float* w,
                           uint16_t* out, hipStream_t stream);
+
+// Low-latency path limits: T * k pairs, experts (LDS counters), picks
+constexpr int kMaxPairsLL = 8192;
+constexpr int kMaxExpertsLL = 1024;
+constexpr int kMaxTopkLL = 32;
+
+hipError_t launch_dispatch_ll(const Shape& s, int cap, bool fp8, const uint16_t* x, const int32_t* topk_idx,
+                              void* recv, float* recv_scales, int32_t* recv_count, int32_t* recv_src,
+                              int32_t* slot, hipStream_t stream);
 
 // Grid of the row kernels (dispatch, combine): one-wave workgroups, each
 // taking one 64-lane piece of a token's row (`segs` pieces per row) per

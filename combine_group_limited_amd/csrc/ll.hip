@@ -1,0 +1,125 @@
+// ll.hip -- low-latency dispatch: each token goes straight into
+// fixed-capacity receive rows of its experts, with no separate layout pass
+// and nothing for the host to wait for.
+//
+// The DeepEP pages describe a second kernel family for latency-sensitive
+// inference decoding (news report on the release, feature list; blog
+// "【Day2】DeepEP ...", "DeepEP的关键技术" item 4 and "DeepEP 的性能表现",
+// low-latency kernels at 128 tokens per batch, FP8 dispatch, BF16 combine).
+// The reading implemented here: expert e owns receive rows
+// [e * cap, (e + 1) * cap); pair (t, j) routed to e takes row e * cap + pos,
+// where pos counts the routed pairs before it (row-major (t, j) order) with
+// the same expert -- the same in-expert order as the normal layout -- and
+// is dropped (slot -1) when pos >= cap.
+//
+// One workgroup per token: its waves share the count of earlier pairs per
+// pick (ballots over 64 entries at a time, summed in LDS), then store the
+// token's row pieces as the normal dispatch does (rows.h).  One extra
+// workgroup writes the per-expert counts.  The work to find positions grows
+// with T * k, so the path is limited to small batches (decode).
+#include "launch.h"
+#include "rows.h"
+
+namespace ep {
+
+namespace {
+
+constexpr int kMaxBlockThreads = 1024;
+
+template <bool FP8>
+__global__ __launch_bounds__(kMaxBlockThreads) void dispatch_ll_kernel(
+    const uint16_t* __restrict__ x, const int32_t* __restrict__ idx, void* __restrict__ recv,
+    float* __restrict__ recv_sc, int32_t* __restrict__ recv_count, int32_t* __restrict__ recv_src,
+    int32_t* __restrict__ slot_out, int T, int H, int E, int k, int cap) {
+    __shared__ int s_cnt[kMaxExpertsLL];  // expert counts (last block) or per-pick counts
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int nw = blockDim.x >> 6;
+
+    if (blockIdx.x == (unsigned)T) {  // per-expert counts of routed pairs
+        const int P = T * k;
+        for (int i = tid; i < E; i += blockDim.x) s_cnt[i] = 0;
+        __syncthreads();
+        for (int p = tid; p < P; p += blockDim.x) {
+            const int e = idx[p];
+            if ((unsigned)e < (unsigned)E) atomicAdd(&s_cnt[e], 1);
+        }
+        __syncthreads();
+        for (int i = tid; i < E; i += blockDim.x) recv_count[i] = s_cnt[i];
+        return;
+    }
+
+    const int t = blockIdx.x;
+    if (tid < kMaxTopkLL) s_cnt[tid] = 0;
+    int my_e = -1;  // lane j < k: expert of pick j, -1 if unrouted
+    if (lane < k) {
+        const int v = idx[(size_t)t * k + lane];
+        my_e = (unsigned)v < (unsigned)E ? v : -1;
+    }
+    __syncthreads();
+
+    // routed pairs of earlier tokens with the same expert, per pick: the
+    // entries [0, t*k) in chunks of 64, four chunks per wave in flight
+    const int before = t * k;
+    int part = 0;
+    for (int c0 = wave * 4; c0 * 64 < before; c0 += nw * 4) {
+        int v[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int p = (c0 + u) * 64 + lane;
+            v[u] = p < before ? idx[p] : -1;
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            for (int j = 0; j < k; ++j) {
+                const int ej = __builtin_amdgcn_readlane(my_e, j);
+                const uint64_t m = __ballot(ej >= 0 && v[u] == ej);
+                part += (lane == j) ? __popcll(m) : 0;
+            }
+        }
+    }
+    if (lane < k && part > 0) atomicAdd(&s_cnt[lane], part);
+    __syncthreads();
+    int my_pos = lane < k ? s_cnt[lane] : 0;
+    // earlier picks of this token with the same expert (a repeated expert)
+    for (int j = 0; j + 1 < k; ++j) {
+        const int ej = __builtin_amdgcn_readlane(my_e, j);
+        my_pos += (lane > j && lane < k && my_e >= 0 && my_e == ej) ? 1 : 0;
+    }
+    const int my_slot = (my_e >= 0 && my_pos < cap) ? my_e * cap + my_pos : -1;
+    if (wave == 0 && lane < k) {
+        slot_out[(size_t)t * k + lane] = my_slot;
+        if (my_slot >= 0) recv_src[my_slot] = t;
+    }
+
+    const int nrows = E * cap;
+    const uint16_t* xrow = x + (size_t)t * H;
+    if (FP8) {
+        // 8-lane scale blocks stay together: H/16 and blockDim are multiples of 8
+        for (int chunk = tid; chunk < (H >> 4); chunk += blockDim.x)
+            fp8_piece(xrow, chunk, H, k, my_slot, nrows, static_cast<uint8_t*>(recv), recv_sc);
+    } else {
+        for (int chunk = tid; chunk < (H >> 3); chunk += blockDim.x)
+            bf16_piece(xrow, chunk, H, k, my_slot, nrows, static_cast<uint16_t*>(recv));
+    }
+}
+
+}  // namespace
+
+hipError_t launch_dispatch_ll(const Shape& s, int cap, bool fp8, const uint16_t* x, const int32_t* topk_idx,
+                              void* recv, float* recv_scales, int32_t* recv_count, int32_t* recv_src,
+                              int32_t* slot, hipStream_t stream) {
+    const int lanes = fp8 ? (s.H >> 4) : (s.H >> 3);
+    int threads = (lanes + 63) / 64 * 64;
+    if (threads > kMaxBlockThreads) threads = kMaxBlockThreads;
+    if (fp8)
+        hipLaunchKernelGGL(dispatch_ll_kernel<true>, dim3(s.T + 1), dim3(threads), 0, stream, x, topk_idx, recv,
+                           recv_scales, recv_count, recv_src, slot, s.T, s.H, s.E, s.k, cap);
+    else
+        hipLaunchKernelGGL(dispatch_ll_kernel<false>, dim3(s.T + 1), dim3(threads), 0, stream, x, topk_idx, recv,
+                           recv_scales, recv_count, recv_src, slot, s.T, s.H, s.E, s.k, cap);
+    return hipGetLastError();
+}
+
+}  // namespace ep

@@ -185,6 +185,46 @@ EP_API int ep_combine(const ep_config_t* cfg, const void* y,
                       const int32_t* slot, const float* topk_w, void* out,
                       void* stream);
 
+/* Low-latency dispatch ([NEWS] feature list: low-latency kernels for
+ * inference decoding; [DAY2] "DeepEP的关键技术" item 4 and "DeepEP 的性能表现":
+ * 128 tokens per batch, FP8 dispatch, BF16 combine).  One kernel, no layout
+ * pass: expert e owns `capacity` receive rows [e*capacity, (e+1)*capacity),
+ * and routed pair (t, j) with expert e takes row e*capacity + pos, where pos
+ * is the number of routed pairs before it in row-major (t, j) order with
+ * the same expert (the in-expert order of ep_get_layout).  Pairs with
+ * pos >= capacity are dropped (slot -1); capacity = T never drops a pair of
+ * ep_route's output (it never repeats an expert within a token).
+ *   x            device, bf16 [T, H], 16-byte aligned
+ *   topk_idx     device, int32 [T, k]; entries outside [0, E) are unrouted
+ *   capacity     rows per expert, >= 1, E * capacity < 2^31
+ *   recv_dtype   EP_RECV_FP8_E4M3 or EP_RECV_BF16
+ *   recv         device, [E * capacity, H] e4m3 codes or bf16, 16-byte
+ *                aligned; rows no pair takes are not written
+ *   recv_scales  device, fp32 [E * capacity, H/128] for FP8, NULL for BF16
+ *   recv_count   device, int32 [E] out: routed pairs per expert (may exceed
+ *                capacity; rows written = min(count, capacity))
+ *   recv_src     device, int32 [E * capacity] out: token of each written
+ *                row; other entries are not written
+ *   slot         device, int32 [T, k] out: receive row of each pair, or -1
+ * Payload arithmetic as ep_dispatch.  Limit: T * k <= 8192 (finding the
+ * positions inside the dispatch costs O(T * k) per token), else
+ * EP_ERR_UNSUPPORTED.  Alignment: 4 bytes for the int32 arrays. */
+EP_API int ep_dispatch_ll(const ep_config_t* cfg, const void* x, const int32_t* topk_idx, int32_t capacity,
+                          int recv_dtype, void* recv, float* recv_scales, int32_t* recv_count,
+                          int32_t* recv_src, int32_t* slot, void* stream);
+
+/* Low-latency combine: ep_combine over expert outputs y laid out as
+ * ep_dispatch_ll's receive rows.
+ *   capacity  as passed to ep_dispatch_ll
+ *   y         device, bf16 [E * capacity, H], 16-byte aligned
+ *   slot      device, int32 [T, k] from ep_dispatch_ll; entries outside
+ *             [0, E * capacity) are skipped
+ *   topk_w    device, fp32 [T, k]
+ *   out       device, bf16 [T, H], 16-byte aligned
+ * Arithmetic as ep_combine. */
+EP_API int ep_combine_ll(const ep_config_t* cfg, int32_t capacity, const void* y, const int32_t* slot,
+                         const float* topk_w, void* out, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

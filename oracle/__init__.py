@@ -60,6 +60,7 @@ def lib() -> ctypes.CDLL:
         L.orc_select.argtypes = [I, I, I, I, I, I, P, P, P]; L.orc_select.restype = I
         L.orc_route.argtypes = [I, I, I, I, I, I, P, P, P]; L.orc_route.restype = I
         L.orc_layout.argtypes = [I, I, I, I, P, P, P, P, P, P]; L.orc_layout.restype = I
+        L.orc_ll_layout.argtypes = [I, I, I, I, P, P, P, P]; L.orc_ll_layout.restype = I
         L.orc_dispatch_fp8.argtypes = [I, I, I, I, P, P, P, P]; L.orc_dispatch_fp8.restype = None
         L.orc_dispatch_bf16.argtypes = [I, I, I, I, P, P, P]; L.orc_dispatch_bf16.restype = None
         L.orc_combine.argtypes = [I, I, I, I, P, P, P, P]; L.orc_combine.restype = None
@@ -165,6 +166,23 @@ def layout(topk_idx, E: int, R: int):
     if rc != 0:
         raise ValueError("invalid layout configuration")
     return dict(cnt=cnt, off=off, ntok_rank=ntok, slot=slot, recv_token=recv_token)
+
+
+def ll_layout(topk_idx, E: int, cap: int, src=None):
+    """Low-latency layout: returns dict(count [E], slot [T, k], src [E*cap]);
+    src entries of rows no pair takes keep the given array's values (-1 if
+    none is given)."""
+    idx = _c(topk_idx, np.int32)
+    T, k = idx.shape
+    count = np.empty(E, np.int32)
+    slot = np.empty((T, k), np.int32)
+    if src is None:
+        src = np.full(E * cap, -1, np.int32)
+    src = _c(src, np.int32)
+    rc = lib().orc_ll_layout(T, k, E, cap, _p(idx), _p(count), _p(slot), _p(src))
+    if rc != 0:
+        raise ValueError("invalid low-latency layout configuration")
+    return dict(count=count, slot=slot, src=src)
 
 
 def dispatch_fp8(x_bf16, slot, nrows: int, q=None, sc=None):

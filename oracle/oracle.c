@@ -260,6 +260,33 @@ int orc_layout(int T, int k, int E, int R, const int32_t* topk_idx,
 }
 
 /* ---------------------------------------------------------------------------
+ * Low-latency receive layout: fixed rows per expert, positions in the order
+ * the pairs are met (row-major), overflow dropped.
+ * ------------------------------------------------------------------------- */
+int orc_ll_layout(int T, int k, int E, int cap, const int32_t* topk_idx,
+                  int32_t* count, int32_t* slot, int32_t* src) {
+    if (T < 0 || k < 1 || E < 1 || cap < 1) return -1;
+    long P = (long)T * k;
+    for (int e = 0; e < E; ++e) count[e] = 0;
+    for (long p = 0; p < P; ++p) {
+        int e = topk_idx[p];
+        if (e < 0 || e >= E) {
+            slot[p] = -1;
+            continue;
+        }
+        int pos = count[e];
+        count[e] += 1;
+        if (pos < cap) {
+            slot[p] = e * cap + pos;
+            src[(long)e * cap + pos] = (int32_t)(p / k);
+        } else {
+            slot[p] = -1;
+        }
+    }
+    return 0;
+}
+
+/* ---------------------------------------------------------------------------
  * Dispatch.  Sends each token to the experts its gate picked ([DAY2]
  * "DeepEP是什么"; [NEWS] feature list), with an FP8 payload for dispatch
  * ([NEWS] "具体性能方面").  Readings: E4M3 codes with one fp32 scale per

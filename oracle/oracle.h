@@ -93,6 +93,19 @@ int orc_layout(int T, int k, int E, int R, const int32_t* topk_idx,
                int32_t* cnt, int32_t* off, int32_t* ntok_rank, int32_t* slot,
                int32_t* recv_token);
 
+/* Low-latency receive layout ([NEWS] feature list and [DAY2]
+ * "DeepEP的关键技术": low-latency kernels for decoding; the layout is this
+ * library's reading).  Expert e owns `cap` receive rows [e*cap, (e+1)*cap).
+ * Going through the routed pairs (t, j) in row-major order, the pair's
+ * position pos is the number of routed pairs already seen with the same
+ * expert; it takes row e*cap + pos when pos < cap and is dropped otherwise.
+ *   count[e]   routed pairs with expert e (all of them, dropped or not)   (E)
+ *   slot[t,j]  e*cap + pos, or -1 when unrouted or dropped            (T x k)
+ *   src[row]   token of each taken row; other entries untouched     (E*cap)
+ * Returns 0, or -1 on an invalid configuration. */
+int orc_ll_layout(int T, int k, int E, int cap, const int32_t* topk_idx,
+                  int32_t* count, int32_t* slot, int32_t* src);
+
 /* FP8 dispatch.  For each token t and 128-channel block b of x (T x H bf16):
  *   amax = max |x|,  a = max(amax, 1e-4),  inv = 448 / a,  sc = a / 448,
  *   q = e4m3(x * inv);

@@ -137,6 +137,34 @@ def test_combine_rejections():
     assert lib.ep_combine(ctypes.byref(z), None, None, None, None, None) == L.EP_OK
 
 
+def test_low_latency_rejections():
+    lib = ep.lib()
+    c = _cfg(T=128).c()
+    F8, B16 = L.EP_RECV_FP8_E4M3, L.EP_RECV_BF16
+    ok = [FAKE, FAKE, 128, F8, FAKE, FAKE, FAKE, FAKE, FAKE, None]
+    def call(cfg, *over):
+        a = list(ok)
+        for i, v in over:
+            a[i] = v
+        return lib.ep_dispatch_ll(ctypes.byref(cfg), *a)
+    assert call(c, (2, 0)) == L.EP_ERR_INVALID_ARG                    # capacity 0
+    assert call(c, (2, 1 << 23)) == L.EP_ERR_INVALID_ARG              # E * capacity >= 2^31
+    assert call(c, (3, 5)) == L.EP_ERR_INVALID_ARG                    # unknown payload type
+    assert call(c, (6, None)) == L.EP_ERR_INVALID_ARG                 # no recv_count
+    assert call(c, (5, None)) == L.EP_ERR_INVALID_ARG                 # FP8 without scales
+    assert call(c, (3, B16)) == L.EP_ERR_INVALID_ARG                  # BF16 with scales
+    assert call(c, (7, None)) == L.EP_ERR_INVALID_ARG                 # no recv_src
+    assert call(c, (0, FAKE + 8)) == L.EP_ERR_ALIGNMENT
+    assert call(c, (8, FAKE + 2)) == L.EP_ERR_ALIGNMENT
+    big = _cfg(T=1025).c()                                           # T * k > 8192
+    assert call(big) == L.EP_ERR_UNSUPPORTED
+    assert lib.ep_combine_ll(ctypes.byref(c), 0, FAKE, FAKE, FAKE, FAKE, None) == L.EP_ERR_INVALID_ARG
+    assert lib.ep_combine_ll(ctypes.byref(c), 128, FAKE, FAKE, FAKE, None, None) == L.EP_ERR_INVALID_ARG
+    assert lib.ep_combine_ll(ctypes.byref(c), 128, FAKE + 4, FAKE, FAKE, FAKE, None) == L.EP_ERR_ALIGNMENT
+    z = _cfg(T=0).c()
+    assert lib.ep_combine_ll(ctypes.byref(z), 4, None, None, None, None, None) == L.EP_OK
+
+
 def test_binding_rejects_cpu_tensors():
     import torch
     w = W.TINY
