@@ -98,8 +98,11 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default=None,
                     help="workload (default: prefill for the normal path, decode for the low-latency path)")
-    ap.add_argument("--path", choices=("normal", "ll"), default="normal",
-                    help="normal: route + layout + dispatch + combine; ll: route + dispatch_ll + combine_ll")
+    ap.add_argument("--path", choices=("normal", "ll", "overlap"), default="normal",
+                    help="normal: route + layout + dispatch + combine; ll: route + dispatch_ll + combine_ll; "
+                         "overlap: dispatch + combine on a CU budget next to a bf16 GEMM on the other CUs")
+    ap.add_argument("--cus", default="32,64,128,192", help="CU budgets of the overlap path")
+    ap.add_argument("--gemm-n", type=int, default=14336, help="output width of the overlap path's GEMM")
     ap.add_argument("--recv-dtype", choices=("fp8", "bf16"), default="fp8", help="dispatch payload")
     ap.add_argument("--capacity", type=int, default=0, help="low-latency rows per expert (0: T)")
     ap.add_argument("--sets", type=int, default=0,
@@ -402,6 +405,121 @@ def run_ll(args, w):
     return rec
 
 
+def run_overlap(args, w):
+    """Dispatch + combine confined to CUs [0, N) (ep_stream_create_cu_range)
+    while a stand-in compute stream runs bf16 GEMMs (hipBLASLt through
+    torch.matmul, [T, H] x [H, gemm_n], by default an expert up-projection of
+    width 2 x 7168) on CUs [N, all): each alone, then both at once, for each
+    budget N."""
+    import numpy as np
+    import torch
+
+    import combine_group_limited_amd as ep
+    from combine_group_limited_amd import _lib as L
+    import workloads as W
+
+    cfg = ep.Config.of(w)
+    dev = torch.device("cuda", 0)
+    ncu = torch.cuda.get_device_properties(0).multi_processor_count
+    dc_bytes = w.bytes_dispatch_fp8() + w.bytes_combine()
+    nsets = buffer_sets(args.sets, dc_bytes, dc_bytes)
+    lg = torch.from_numpy(W.gen_logits(w)).to(dev)
+    idx, wt = ep.route(cfg, lg)
+    slot = ep.get_layout(cfg, idx)["slot"]
+    x0 = torch.from_numpy(W.gen_x(w).view(np.int16)).view(torch.bfloat16).to(dev)
+    y0 = torch.from_numpy(W.gen_y(w).view(np.int16)).view(torch.bfloat16).to(dev)
+    sets = [dict(x=x0 if i == 0 else x0.clone(), y=y0 if i == 0 else y0.clone(),
+                 recv=torch.empty((w.nrows, w.H), dtype=torch.uint8, device=dev),
+                 scales=torch.empty((w.nrows, w.H // 128), dtype=torch.float32, device=dev),
+                 out=torch.empty((w.T, w.H), dtype=torch.bfloat16, device=dev)) for i in range(nsets)]
+    gn = args.gemm_n
+    A = torch.randn((w.T, w.H), device=dev).to(torch.bfloat16)
+    B = torch.randn((w.H, gn), device=dev).to(torch.bfloat16)
+    C = torch.empty((w.T, gn), dtype=torch.bfloat16, device=dev)
+    gemm_flop = 2.0 * w.T * w.H * gn
+    lib = L.lib()
+    c = cfg.c()
+    cp = ctypes.byref(c)
+    ptr = [{k: v.data_ptr() for k, v in b.items()} for b in sets]
+    torch.cuda.synchronize()
+
+    def dc(i, sh):
+        p = ptr[i % nsets]
+        if lib.ep_dispatch(cp, p["x"], slot.data_ptr(), L.EP_RECV_FP8_E4M3, p["recv"], p["scales"], sh) != 0:
+            raise RuntimeError("ep_dispatch failed")
+        if lib.ep_combine(cp, p["y"], slot.data_ptr(), wt.data_ptr(), p["out"], sh) != 0:
+            raise RuntimeError("ep_combine failed")
+
+    def gemm(i, sh):
+        torch.matmul(A, B, out=C)
+
+    hev = HipEvents()
+    n = max(args.steps, 1)
+
+    def alone(stream, fn):
+        sh = stream.cuda_stream
+        with torch.cuda.stream(stream.torch):
+            for i in range(max(args.warmup, 1)):
+                fn(i, sh)
+            torch.cuda.synchronize()
+            e = hev.create(2)
+            hev.record(e[0], sh)
+            for i in range(n):
+                fn(i, sh)
+            hev.record(e[1], sh)
+            t = hev.seconds(e[0], e[1]) / n
+            hev.destroy(e)
+        return t
+
+    def together(sc, sg):
+        e = hev.create(4)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        hev.record(e[0], sc.cuda_stream)
+        hev.record(e[2], sg.cuda_stream)
+        for i in range(n):  # interleave the issue so both queues stay fed
+            with torch.cuda.stream(sg.torch):
+                gemm(i, sg.cuda_stream)
+            dc(i, sc.cuda_stream)
+        hev.record(e[1], sc.cuda_stream)
+        hev.record(e[3], sg.cuda_stream)
+        torch.cuda.synchronize()
+        wall = (time.perf_counter() - t0) / n
+        r = hev.seconds(e[0], e[1]) / n, hev.seconds(e[2], e[3]) / n, wall
+        hev.destroy(e)
+        return r
+
+    with ep.CuRangeStream(0, ncu) as full:
+        dc_full, gemm_full = alone(full, dc), alone(full, gemm)
+    rows = []
+    for N in [int(v) for v in args.cus.split(",") if v.strip()]:
+        if not 0 < N < ncu:
+            continue
+        with ep.CuRangeStream(0, N) as sc, ep.CuRangeStream(N, ncu - N) as sg:
+            dca, ga = alone(sc, dc), alone(sg, gemm)
+            dco, go, wall = together(sc, sg)
+        rows.append({"comm_cus": N, "compute_cus": ncu - N,
+                     "dc_alone_us": round(dca * 1e6, 2), "gemm_alone_us": round(ga * 1e6, 2),
+                     "dc_overlapped_us": round(dco * 1e6, 2), "gemm_overlapped_us": round(go * 1e6, 2),
+                     "wall_per_pair_us": round(wall * 1e6, 2),
+                     "dc_overlapped_gbs": round(dc_bytes / dco / 1e9, 1),
+                     "gemm_overlapped_tflops": round(gemm_flop / go / 1e12, 1),
+                     "serial_full_gpu_us": round((dc_full + gemm_full) * 1e6, 2)})
+    return {
+        "metric": "dispatch+combine on a CU budget overlapped with a bf16 GEMM on the other CUs",
+        "value": None if not rows else min(r["wall_per_pair_us"] for r in rows),
+        "unit": "us per (dispatch+combine, GEMM) pair, best budget",
+        "n_gpus": 1, "steps": n, "warmup": args.warmup, "higher_is_better": False, "scaling": "weak",
+        "vs_baseline": None, "dtype": "fp32", "data": "synthetic",
+        "config": {"workload": w.name, "path": "overlap", "tokens": w.T, "hidden": w.H, "topk": w.k,
+                   "gemm": "bf16 [%d, %d] x [%d, %d] (torch.matmul)" % (w.T, w.H, w.H, gn), "cus": ncu,
+                   "buffer_sets": nsets},
+        "full_gpu": {"dc_us": round(dc_full * 1e6, 2), "gemm_us": round(gemm_full * 1e6, 2),
+                     "gemm_tflops": round(gemm_flop / gemm_full / 1e12, 1)},
+        "budgets": rows,
+    }
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -417,7 +535,8 @@ def main():
     name = args.config or ("decode" if args.path == "ll" else "prefill")
     w = W.CONFIGS[name]
     torch.cuda.set_device(0)
-    rec = run_ll(args, w) if args.path == "ll" else run_normal(args, w)
+    runner = {"normal": run_normal, "ll": run_ll, "overlap": run_overlap}[args.path]
+    rec = runner(args, w)
     print(json.dumps(rec), flush=True)
     return 0
 

@@ -6,6 +6,7 @@ behind the C ABI of include/ep.h); this package is its Python binding.
 from ._lib import EXPORTS, LIB_PATH, lib  # noqa: F401
 from .api import (  # noqa: F401
     Config,
+    CuRangeStream,
     EpError,
     combine,
     combine_ll,

@@ -40,6 +40,8 @@ EXPORTS = (
     "ep_combine",
     "ep_dispatch_ll",
     "ep_combine_ll",
+    "ep_stream_create_cu_range",
+    "ep_stream_destroy",
 )
 
 
@@ -95,5 +97,9 @@ def lib() -> ctypes.CDLL:
         L.ep_dispatch_ll.restype = I
         L.ep_combine_ll.argtypes = [C, I32, P, P, P, P, P]
         L.ep_combine_ll.restype = I
+        L.ep_stream_create_cu_range.argtypes = [I, I, ctypes.POINTER(P)]
+        L.ep_stream_create_cu_range.restype = I
+        L.ep_stream_destroy.argtypes = [P]
+        L.ep_stream_destroy.restype = I
         _lib = L
         return _lib

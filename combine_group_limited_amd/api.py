@@ -250,3 +250,33 @@ def combine_ll(cfg: Config, capacity: int, y: torch.Tensor, slot: torch.Tensor, 
     _check(L.lib().ep_combine_ll(ctypes.byref(c), capacity, _ptr(y), _ptr(slot), _ptr(topk_w), _ptr(out),
                                  _stream(stream, dev)), "ep_combine_ll")
     return out
+
+
+class CuRangeStream:
+    """A HIP stream confined to compute units [first_cu, first_cu + num_cus)
+    (ep_stream_create_cu_range), usable as `stream=` here and, through
+    `.torch`, as a torch stream.  Release it with close() (or a with-block)
+    after its work has been waited for."""
+
+    def __init__(self, first_cu: int, num_cus: int):
+        h = ctypes.c_void_p()
+        _check(L.lib().ep_stream_create_cu_range(first_cu, num_cus, ctypes.byref(h)), "ep_stream_create_cu_range")
+        self.handle = h.value
+        self.first_cu, self.num_cus = first_cu, num_cus
+        self.torch = torch.cuda.ExternalStream(self.handle)
+
+    @property
+    def cuda_stream(self) -> int:
+        return self.handle
+
+    def close(self) -> None:
+        if self.handle:
+            _check(L.lib().ep_stream_destroy(self.handle), "ep_stream_destroy")
+            self.handle = None
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        torch.cuda.synchronize()
+        self.close()

@@ -225,6 +225,26 @@ EP_API int ep_dispatch_ll(const ep_config_t* cfg, const void* x, const int32_t* 
 EP_API int ep_combine_ll(const ep_config_t* cfg, int32_t capacity, const void* y, const int32_t* slot,
                          const float* topk_w, void* out, void* stream);
 
+/* CU budget ([GH#6] "Technical Overview of DeepEP": SM-count control; [DAY2]
+ * "All-to-All通信": communication kernels confined to a few SMs and
+ * overlapped with the compute stream).  Creates a HIP stream whose kernels
+ * run only on compute units [first_cu, first_cu + num_cus) of the current
+ * device; pass it as `stream` to the calls above to cap the CUs they use,
+ * and give the remaining CUs to a compute stream made the same way.  The
+ * stream has the default priority.  On MI355X the HIP runtime accepts only
+ * contiguous CU ranges.
+ *   first_cu, num_cus  0 <= first_cu, num_cus >= 1,
+ *                      first_cu + num_cus <= the device's CU count
+ *   stream             host, out: the new hipStream_t
+ * Returns EP_ERR_INVALID_ARG for a bad range (no HIP call is made for a
+ * negative or empty one) and EP_ERR_HIP if the runtime refuses the stream.
+ * The caller owns the stream and releases it with ep_stream_destroy. */
+EP_API int ep_stream_create_cu_range(int first_cu, int num_cus, void** stream);
+
+/* Destroys a stream made by ep_stream_create_cu_range (after the work on it
+ * has been waited for, as for hipStreamDestroy). */
+EP_API int ep_stream_destroy(void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -165,6 +165,16 @@ def test_low_latency_rejections():
     assert lib.ep_combine_ll(ctypes.byref(z), 4, None, None, None, None, None) == L.EP_OK
 
 
+def test_cu_range_stream_rejections():
+    lib = ep.lib()
+    h = ctypes.c_void_p()
+    # rejected before any HIP call
+    assert lib.ep_stream_create_cu_range(0, 0, ctypes.byref(h)) == L.EP_ERR_INVALID_ARG
+    assert lib.ep_stream_create_cu_range(-1, 8, ctypes.byref(h)) == L.EP_ERR_INVALID_ARG
+    assert lib.ep_stream_create_cu_range(0, 8, None) == L.EP_ERR_INVALID_ARG
+    assert lib.ep_stream_destroy(None) == L.EP_ERR_INVALID_ARG
+
+
 def test_binding_rejects_cpu_tensors():
     import torch
     w = W.TINY
