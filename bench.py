@@ -98,9 +98,10 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default=None,
                     help="workload (default: prefill for the normal path, decode for the low-latency path)")
-    ap.add_argument("--path", choices=("normal", "ll", "overlap"), default="normal",
+    ap.add_argument("--path", choices=("normal", "ll", "overlap", "dedup"), default="normal",
                     help="normal: route + layout + dispatch + combine; ll: route + dispatch_ll + combine_ll; "
-                         "overlap: dispatch + combine on a CU budget next to a bf16 GEMM on the other CUs")
+                         "overlap: dispatch + combine on a CU budget next to a bf16 GEMM on the other CUs; "
+                         "dedup: per-rank deduplicated dispatch + in-rank partial combine + combine of partials")
     ap.add_argument("--cus", default="32,64,128,192", help="CU budgets of the overlap path")
     ap.add_argument("--gemm-n", type=int, default=14336, help="output width of the overlap path's GEMM")
     ap.add_argument("--recv-dtype", choices=("fp8", "bf16"), default="fp8", help="dispatch payload")
@@ -520,6 +521,117 @@ def run_overlap(args, w):
     }
 
 
+def run_dedup(args, w):
+    """route + layout + rank layout + deduplicated FP8 dispatch (one row per
+    (token, rank)) + in-rank partial combine + combine of the partial rows,
+    on resident buffers."""
+    import numpy as np
+    import torch
+
+    import combine_group_limited_amd as ep
+    from combine_group_limited_amd import _lib as L
+    import workloads as W
+    import oracle  # only to count the rank rows of the seeded routing for the byte model
+
+    cfg = ep.Config.of(w)
+    dev = torch.device("cuda", 0)
+    lg_np, x_np, y_np = W.gen_logits(w), W.gen_x(w), W.gen_y(w)
+    idx_np, _ = oracle.route(lg_np, w.G, w.TG, w.k, w.topm)
+    rows = int(oracle.rank_layout(idx_np, w.E, w.R)["rank_offset"][-1])
+    B = w.H // 128
+    P = w.T * w.k
+    bytes_ = dict(route=w.bytes_route(), layout=w.bytes_layout(),
+                  rank_layout=P * 8 + 4 * (2 * w.R + 1),
+                  dispatch=w.T * 2 * w.H + rows * (w.H + 4 * B) + 4 * P,
+                  partial=2 * w.H * P + 2 * w.H * rows + 16 * P,
+                  combine_ranks=2 * w.H * rows + 2 * w.H * w.T + 4 * P)
+    touched = sum(bytes_.values())
+    nsets = buffer_sets(args.sets, touched, touched)
+    logits0 = torch.from_numpy(lg_np).to(dev)
+    x0 = torch.from_numpy(x_np.view(np.int16)).view(torch.bfloat16).to(dev)
+    y0 = torch.from_numpy(y_np.view(np.int16)).view(torch.bfloat16).to(dev)
+    i32 = dict(dtype=torch.int32, device=dev)
+    ws = torch.empty(max(256, ep.layout_workspace_bytes(cfg)), dtype=torch.uint8, device=dev)
+    rws = torch.empty(max(256, ep.rank_layout_workspace_bytes(cfg)), dtype=torch.uint8, device=dev)
+    sets = []
+    for i in range(nsets):
+        sets.append(dict(
+            logits=logits0 if i == 0 else logits0.clone(), x=x0 if i == 0 else x0.clone(),
+            y=y0 if i == 0 else y0.clone(),
+            idx=torch.empty((w.T, w.k), **i32), wt=torch.empty((w.T, w.k), dtype=torch.float32, device=dev),
+            cnt=torch.empty(w.E, **i32), ntok=torch.empty(w.R, **i32), off=torch.empty(w.E + 1, **i32),
+            slot=torch.empty((w.T, w.k), **i32),
+            rcnt=torch.empty(w.R, **i32), roff=torch.empty(w.R + 1, **i32), rslot=torch.empty((w.T, w.k), **i32),
+            recv=torch.empty((P, w.H), dtype=torch.uint8, device=dev),
+            scales=torch.empty((P, B), dtype=torch.float32, device=dev),
+            partial=torch.empty((P, w.H), dtype=torch.bfloat16, device=dev),
+            out=torch.empty((w.T, w.H), dtype=torch.bfloat16, device=dev)))
+    for b in sets:
+        ep.route(cfg, b["logits"], b["idx"], b["wt"])
+        ep.get_layout(cfg, b["idx"], dict(cnt=b["cnt"], ntok_rank=b["ntok"], off=b["off"], slot=b["slot"]), ws,
+                      with_recv_token=False)
+        ep.get_rank_layout(cfg, b["idx"], dict(rank_count=b["rcnt"], rank_offset=b["roff"], rank_slot=b["rslot"]),
+                           rws, with_rank_token=False)
+        ep.dispatch(cfg, b["x"], b["rslot"], "fp8", b["recv"], b["scales"])
+        ep.combine_rank_partial(cfg, b["y"], b["idx"], b["slot"], b["wt"], b["rslot"], b["partial"])
+        ep.combine_ranks(cfg, b["partial"], b["rslot"], b["out"])
+    torch.cuda.synchronize()
+    assert int(sets[0]["roff"][-1]) == rows
+    ptr = [{k: v.data_ptr() for k, v in b.items()} for b in sets]
+    lib = L.lib()
+    c = cfg.c()
+    cp = ctypes.byref(c)
+    sh = int(torch.cuda.current_stream().cuda_stream)
+
+    def check(rc, name):
+        if rc != 0:
+            raise RuntimeError("%s failed: %s" % (name, lib.ep_strerror(rc).decode()))
+
+    def launch(i, rec):
+        p = ptr[i]
+        rec(0)
+        check(lib.ep_route(cp, p["logits"], p["idx"], p["wt"], sh), "ep_route")
+        rec(1)
+        check(lib.ep_get_layout(cp, p["idx"], p["cnt"], p["ntok"], p["off"], p["slot"], None, ws.data_ptr(),
+                                ws.numel(), sh), "ep_get_layout")
+        rec(2)
+        check(lib.ep_get_rank_layout(cp, p["idx"], p["rcnt"], p["roff"], p["rslot"], None, rws.data_ptr(),
+                                     rws.numel(), sh), "ep_get_rank_layout")
+        rec(3)
+        check(lib.ep_dispatch(cp, p["x"], p["rslot"], L.EP_RECV_FP8_E4M3, p["recv"], p["scales"], sh), "ep_dispatch")
+        rec(4)
+        check(lib.ep_combine_rank_partial(cp, p["y"], p["idx"], p["slot"], p["wt"], p["rslot"], p["partial"], sh),
+              "ep_combine_rank_partial")
+        rec(5)
+        check(lib.ep_combine_ranks(cp, p["partial"], p["rslot"], p["out"], sh), "ep_combine_ranks")
+        rec(6)
+
+    stages = ("route", "layout", "rank_layout", "dispatch", "partial", "combine_ranks")
+    dur, wall = timed_steps(args, nsets, launch, stages)
+    kt = kernel_table(dur, bytes_)
+    avg = {s: kt[s]["avg_us"] * 1e-6 for s in stages}
+    moved = bytes_["dispatch"] + bytes_["partial"] + bytes_["combine_ranks"]
+    t_dc = avg["dispatch"] + avg["partial"] + avg["combine_ranks"]
+    # bytes that would cross links between GPUs: payload + scales out, one
+    # bf16 row per (token, rank) back, against one row per (token, expert)
+    link_dedup = rows * (w.H + 4 * B + 2 * w.H)
+    link_flat = P * (w.H + 4 * B + 2 * w.H)
+    return {
+        "metric": "deduplicated dispatch + two-level combine HBM GB/s at %d tok x %d hidden top-%d" % (w.T, w.H, w.k),
+        "value": round(moved / t_dc / 1e9, 1),
+        "unit": "GB/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(wall / args.steps * 1e3, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "fp32", "data": "synthetic",
+        "config": {"workload": w.name, "path": "dedup", "tokens": w.T, "hidden": w.H, "experts": w.E,
+                   "topk": w.k, "virtual_ranks": w.R, "buffer_sets": nsets},
+        "rank_rows": rows, "rank_rows_per_token": round(rows / w.T, 3),
+        "dedup_dispatch_combine_us": round(t_dc * 1e6, 2),
+        "link_bytes": {"flat": link_flat, "dedup": link_dedup, "saved_frac": round(1 - link_dedup / link_flat, 4)},
+        "kernels": kt,
+    }
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -535,7 +647,7 @@ def main():
     name = args.config or ("decode" if args.path == "ll" else "prefill")
     w = W.CONFIGS[name]
     torch.cuda.set_device(0)
-    runner = {"normal": run_normal, "ll": run_ll, "overlap": run_overlap}[args.path]
+    runner = {"normal": run_normal, "ll": run_ll, "overlap": run_overlap, "dedup": run_dedup}[args.path]
     rec = runner(args, w)
     print(json.dumps(rec), flush=True)
     return 0

@@ -10,10 +10,14 @@ from .api import (  # noqa: F401
     EpError,
     combine,
     combine_ll,
+    combine_rank_partial,
+    combine_ranks,
     dispatch,
     dispatch_ll,
     get_layout,
+    get_rank_layout,
     layout_workspace_bytes,
+    rank_layout_workspace_bytes,
     route,
     validate,
 )

@@ -40,6 +40,10 @@ EXPORTS = (
     "ep_combine",
     "ep_dispatch_ll",
     "ep_combine_ll",
+    "ep_rank_layout_workspace_bytes",
+    "ep_get_rank_layout",
+    "ep_combine_rank_partial",
+    "ep_combine_ranks",
     "ep_stream_create_cu_range",
     "ep_stream_destroy",
 )
@@ -97,6 +101,14 @@ def lib() -> ctypes.CDLL:
         L.ep_dispatch_ll.restype = I
         L.ep_combine_ll.argtypes = [C, I32, P, P, P, P, P]
         L.ep_combine_ll.restype = I
+        L.ep_rank_layout_workspace_bytes.argtypes = [C]
+        L.ep_rank_layout_workspace_bytes.restype = ctypes.c_size_t
+        L.ep_get_rank_layout.argtypes = [C, P, P, P, P, P, P, ctypes.c_size_t, P]
+        L.ep_get_rank_layout.restype = I
+        L.ep_combine_rank_partial.argtypes = [C, P, P, P, P, P, P, P]
+        L.ep_combine_rank_partial.restype = I
+        L.ep_combine_ranks.argtypes = [C, P, P, P, P]
+        L.ep_combine_ranks.restype = I
         L.ep_stream_create_cu_range.argtypes = [I, I, ctypes.POINTER(P)]
         L.ep_stream_create_cu_range.restype = I
         L.ep_stream_destroy.argtypes = [P]

@@ -252,6 +252,77 @@ def combine_ll(cfg: Config, capacity: int, y: torch.Tensor, slot: torch.Tensor, 
     return out
 
 
+def rank_layout_workspace_bytes(cfg: Config) -> int:
+    c = cfg.c()
+    return int(L.lib().ep_rank_layout_workspace_bytes(ctypes.byref(c)))
+
+
+def get_rank_layout(cfg: Config, topk_idx: torch.Tensor, out: dict | None = None, workspace=None,
+                    with_rank_token: bool = True, stream=None) -> dict:
+    """Per-rank deduplicated layout: dict with rank_count [R], rank_offset
+    [R+1], rank_slot [T, k] and (if requested) rank_token [T*k], all int32.
+    ep_dispatch with rank_slot as the slot map is the deduplicated
+    dispatch."""
+    dev = topk_idx.device
+    _want(topk_idx, "topk_idx", (cfg.T, cfg.k), torch.int32, None)
+    o = dict(out or {})
+    i32 = dict(dtype=torch.int32, device=dev)
+    o.setdefault("rank_count", torch.empty(cfg.R, **i32))
+    o.setdefault("rank_offset", torch.empty(cfg.R + 1, **i32))
+    o.setdefault("rank_slot", torch.empty((cfg.T, cfg.k), **i32))
+    if with_rank_token:
+        o.setdefault("rank_token", torch.empty(cfg.T * cfg.k, **i32))
+    _want(o["rank_count"], "rank_count", (cfg.R,), torch.int32, dev)
+    _want(o["rank_offset"], "rank_offset", (cfg.R + 1,), torch.int32, dev)
+    _want(o["rank_slot"], "rank_slot", (cfg.T, cfg.k), torch.int32, dev)
+    rt = o.get("rank_token")
+    if rt is not None:
+        _want(rt, "rank_token", (cfg.T * cfg.k,), torch.int32, dev)
+    need = rank_layout_workspace_bytes(cfg)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    if workspace.dtype != torch.uint8 or workspace.device != dev or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous uint8 tensor on %s" % dev)
+    c = cfg.c()
+    _check(L.lib().ep_get_rank_layout(ctypes.byref(c), _ptr(topk_idx), _ptr(o["rank_count"]), _ptr(o["rank_offset"]),
+                                      _ptr(o["rank_slot"]), _ptr(rt), _ptr(workspace), workspace.numel(),
+                                      _stream(stream, dev)), "ep_get_rank_layout")
+    return o
+
+
+def combine_rank_partial(cfg: Config, y: torch.Tensor, topk_idx: torch.Tensor, slot: torch.Tensor,
+                         topk_w: torch.Tensor, rank_slot: torch.Tensor, partial=None, stream=None):
+    """In-rank partial combine: bf16 partial rows [T*k, H] (rows no
+    rank_slot names are left as they were)."""
+    dev = y.device
+    _want(y, "y", (cfg.nrows, cfg.H), torch.bfloat16, None)
+    for name, t in (("topk_idx", topk_idx), ("slot", slot), ("rank_slot", rank_slot)):
+        _want(t, name, (cfg.T, cfg.k), torch.int32, dev)
+    _want(topk_w, "topk_w", (cfg.T, cfg.k), torch.float32, dev)
+    if partial is None:
+        partial = torch.empty((cfg.nrows, cfg.H), dtype=torch.bfloat16, device=dev)
+    _want(partial, "partial", (cfg.nrows, cfg.H), torch.bfloat16, dev)
+    c = cfg.c()
+    _check(L.lib().ep_combine_rank_partial(ctypes.byref(c), _ptr(y), _ptr(topk_idx), _ptr(slot), _ptr(topk_w),
+                                           _ptr(rank_slot), _ptr(partial), _stream(stream, dev)),
+           "ep_combine_rank_partial")
+    return partial
+
+
+def combine_ranks(cfg: Config, partial: torch.Tensor, rank_slot: torch.Tensor, out=None, stream=None):
+    """Sum of each token's partial rows -> bf16 [T, H]."""
+    dev = partial.device
+    _want(partial, "partial", (cfg.nrows, cfg.H), torch.bfloat16, None)
+    _want(rank_slot, "rank_slot", (cfg.T, cfg.k), torch.int32, dev)
+    if out is None:
+        out = torch.empty((cfg.T, cfg.H), dtype=torch.bfloat16, device=dev)
+    _want(out, "out", (cfg.T, cfg.H), torch.bfloat16, dev)
+    c = cfg.c()
+    _check(L.lib().ep_combine_ranks(ctypes.byref(c), _ptr(partial), _ptr(rank_slot), _ptr(out),
+                                    _stream(stream, dev)), "ep_combine_ranks")
+    return out
+
+
 class CuRangeStream:
     """A HIP stream confined to compute units [first_cu, first_cu + num_cus)
     (ep_stream_create_cu_range), usable as `stream=` here and, through

@@ -183,6 +183,54 @@ EP_API int ep_combine_ll(const ep_config_t* cfg, int32_t capacity, const void* y
                                          static_cast<uint16_t*>(out), static_cast<hipStream_t>(stream)));
 }
 
+EP_API size_t ep_rank_layout_workspace_bytes(const ep_config_t* cfg) {
+    if (validate(cfg)) return 0;
+    return ep::rank_layout_workspace_bytes(shape_of(cfg));
+}
+
+EP_API int ep_get_rank_layout(const ep_config_t* cfg, const int32_t* topk_idx, int32_t* rank_count,
+                              int32_t* rank_offset, int32_t* rank_slot, int32_t* rank_token, void* workspace,
+                              size_t workspace_bytes, void* stream) {
+    int rc = validate(cfg);
+    if (rc) return rc;
+    if (!rank_count || !rank_offset) return EP_ERR_INVALID_ARG;
+    if (cfg->num_tokens > 0 && (!topk_idx || !rank_slot)) return EP_ERR_INVALID_ARG;
+    if (!aligned(topk_idx, 4) || !aligned(rank_count, 4) || !aligned(rank_offset, 4) || !aligned(rank_slot, 4) ||
+        !aligned(rank_token, 4))
+        return EP_ERR_ALIGNMENT;
+    const ep::Shape s = shape_of(cfg);
+    const size_t need = ep::rank_layout_workspace_bytes(s);
+    if (!workspace || workspace_bytes < need) return EP_ERR_WORKSPACE;
+    if (!aligned(workspace, 256)) return EP_ERR_ALIGNMENT;
+    return hip_status(ep::launch_rank_layout(s, topk_idx, rank_count, rank_offset, rank_slot, rank_token, workspace,
+                                             static_cast<hipStream_t>(stream)));
+}
+
+EP_API int ep_combine_rank_partial(const ep_config_t* cfg, const void* y, const int32_t* topk_idx,
+                                   const int32_t* slot, const float* topk_w, const int32_t* rank_slot,
+                                   void* partial, void* stream) {
+    int rc = validate(cfg);
+    if (rc) return rc;
+    if (cfg->num_tokens > 0 && (!y || !topk_idx || !slot || !topk_w || !rank_slot || !partial))
+        return EP_ERR_INVALID_ARG;
+    if (!aligned(y, 16) || !aligned(partial, 16) || !aligned(topk_idx, 4) || !aligned(slot, 4) ||
+        !aligned(topk_w, 4) || !aligned(rank_slot, 4))
+        return EP_ERR_ALIGNMENT;
+    return hip_status(ep::launch_combine_rank_partial(shape_of(cfg), static_cast<const uint16_t*>(y), topk_idx, slot,
+                                                      topk_w, rank_slot, static_cast<uint16_t*>(partial),
+                                                      static_cast<hipStream_t>(stream)));
+}
+
+EP_API int ep_combine_ranks(const ep_config_t* cfg, const void* partial, const int32_t* rank_slot, void* out,
+                            void* stream) {
+    int rc = validate(cfg);
+    if (rc) return rc;
+    if (cfg->num_tokens > 0 && (!partial || !rank_slot || !out)) return EP_ERR_INVALID_ARG;
+    if (!aligned(partial, 16) || !aligned(out, 16) || !aligned(rank_slot, 4)) return EP_ERR_ALIGNMENT;
+    return hip_status(ep::launch_combine_ranks(shape_of(cfg), static_cast<const uint16_t*>(partial), rank_slot,
+                                               static_cast<uint16_t*>(out), static_cast<hipStream_t>(stream)));
+}
+
 EP_API int ep_stream_create_cu_range(int first_cu, int num_cus, void** stream) {
     if (!stream || first_cu < 0 || num_cus < 1) return EP_ERR_INVALID_ARG;
     int dev = 0, ncu = 0;

@@ -23,6 +23,19 @@ hipError_t launch_layout(const Shape& s, const int32_t* topk_idx, int32_t* cnt, 
                          int32_t* off, int32_t* slot, int32_t* recv_token, void* ws,
                          hipStream_t stream);
 
+// Per-rank deduplicated layout (the layout over "first pick of the token on
+// this rank" entries, one bucket per rank).
+size_t rank_layout_workspace_bytes(const Shape& s);
+hipError_t launch_rank_layout(const Shape& s, const int32_t* topk_idx, int32_t* rank_count, int32_t* rank_offset,
+                              int32_t* rank_slot, int32_t* rank_token, void* ws, hipStream_t stream);
+
+// In-rank partial combine, and the unit-weight combine of partial rows.
+hipError_t launch_combine_rank_partial(const Shape& s, const uint16_t* y, const int32_t* topk_idx,
+                                       const int32_t* slot, const float* w, const int32_t* rank_slot,
+                                       uint16_t* partial, hipStream_t stream);
+hipError_t launch_combine_ranks(const Shape& s, const uint16_t* partial, const int32_t* rank_slot, uint16_t* out,
+                                hipStream_t stream);
+
 hipError_t launch_dispatch_fp8(const Shape& s, const uint16_t* x, const int32_t* slot, uint8_t* recv,
                                float* recv_scales, hipStream_t stream);
 hipError_t launch_dispatch_bf16(const Shape& s, const uint16_t* x, const int32_t* slot, uint16_t* recv,

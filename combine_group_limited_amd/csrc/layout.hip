@@ -193,13 +193,45 @@ hipError_t launch_assign(const Shape& s, long P, int C, const int32_t* idx, cons
     return hipGetLastError();
 }
 
+// Rank layout input: pick p keeps its rank id when it is the first pick of
+// its token on that rank, else -1 (a later pick on the same rank, or an
+// unrouted pick).
+__global__ __launch_bounds__(256) void rank_first_kernel(const int32_t* __restrict__ idx, int32_t* __restrict__ ridx,
+                                                         long P, int k, int E, int EPR) {
+    const long p = (long)blockIdx.x * blockDim.x + threadIdx.x;
+    if (p >= P) return;
+    const int e = idx[p];
+    int out = -1;
+    if ((unsigned)e < (unsigned)E) {
+        const int r = e / EPR;
+        const long t = p / k;
+        const int j = (int)(p - t * k);
+        bool first = true;
+        for (int jj = 0; jj < j; ++jj) {
+            const int e2 = idx[t * k + jj];
+            if ((unsigned)e2 < (unsigned)E && e2 / EPR == r) first = false;
+        }
+        if (first) out = r;
+    }
+    ridx[p] = out;
+}
+
+inline size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
+
+// the layout over rank buckets: one bucket per virtual rank
+inline Shape rank_shape(const Shape& s) {
+    Shape r = s;
+    r.E = s.R;
+    return r;
+}
+
 }  // namespace
 
 size_t layout_workspace_bytes(const Shape& s) {
     const long P = (long)s.T * s.k;
     const int C = layout_blocks(P, layout_waves(s.E));
     const size_t b = (size_t)(s.E + s.R) * (size_t)C * sizeof(int32_t);
-    return (b + 255) & ~(size_t)255;
+    return align256(b);
 }
 
 hipError_t launch_layout(const Shape& s, const int32_t* topk_idx, int32_t* cnt, int32_t* ntok_rank,
@@ -221,6 +253,32 @@ hipError_t launch_layout(const Shape& s, const int32_t* topk_idx, int32_t* cnt, 
     if (e != hipSuccess) return e;
     if (W == 8) return launch_assign<8>(s, P, C, topk_idx, hist, cnt, off, slot, recv_token, stream);
     return launch_assign<4>(s, P, C, topk_idx, hist, cnt, off, slot, recv_token, stream);
+}
+
+// Workspace: the rank-input array [T*k], R scratch counters, then the
+// layout workspace of the rank buckets.
+size_t rank_layout_workspace_bytes(const Shape& s) {
+    const size_t P = (size_t)s.T * s.k;
+    return align256(P * sizeof(int32_t)) + align256((size_t)s.R * sizeof(int32_t)) +
+           layout_workspace_bytes(rank_shape(s));
+}
+
+hipError_t launch_rank_layout(const Shape& s, const int32_t* topk_idx, int32_t* rank_count, int32_t* rank_offset,
+                              int32_t* rank_slot, int32_t* rank_token, void* ws, hipStream_t stream) {
+    const long P = (long)s.T * s.k;
+    char* base = static_cast<char*>(ws);
+    int32_t* ridx = reinterpret_cast<int32_t*>(base);
+    int32_t* ntok = reinterpret_cast<int32_t*>(base + align256((size_t)P * sizeof(int32_t)));
+    void* rest = base + align256((size_t)P * sizeof(int32_t)) + align256((size_t)s.R * sizeof(int32_t));
+    if (P > 0) {
+        hipLaunchKernelGGL(rank_first_kernel, dim3((unsigned)((P + 255) / 256)), dim3(256), 0, stream, topk_idx,
+                           ridx, P, s.k, s.E, s.E / s.R);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    // with one bucket per rank, the per-rank token count the layout also
+    // computes equals the bucket count: it goes to scratch
+    return launch_layout(rank_shape(s), ridx, rank_count, ntok, rank_offset, rank_slot, rank_token, rest, stream);
 }
 
 }  // namespace ep

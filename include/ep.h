@@ -225,6 +225,59 @@ EP_API int ep_dispatch_ll(const ep_config_t* cfg, const void* x, const int32_t* 
 EP_API int ep_combine_ll(const ep_config_t* cfg, int32_t capacity, const void* y, const int32_t* slot,
                          const float* topk_w, void* out, void* stream);
 
+/* Per-rank deduplicated layout ([DAY2] "DeepEP是什么": the normal kernels
+ * send a token once towards each destination and fan it out there;
+ * "All-to-All通信": forward, then accumulate on the way back).  Pick j of
+ * token t is the token's first pick on its virtual rank when no earlier
+ * pick of t is routed to an expert of the same rank.  One receive row per
+ * (token, rank) with a routed pick, rows grouped by rank, tokens ascending
+ * within a rank (the order of ep_get_layout, one level up).
+ *   topk_idx      device, int32 [T, k]; entries outside [0, E) are unrouted
+ *   rank_count    device, int32 [R]     out: rows of rank r (tokens with a
+ *                                       routed pick on r)
+ *   rank_offset   device, int32 [R + 1] out: exclusive prefix sum of
+ *                                       rank_count; [R] = rows in use
+ *   rank_slot     device, int32 [T, k]  out: the (t, rank) row for a first
+ *                                       pick on its rank, else -1
+ *   rank_token    device, int32 [T * k] out (may be NULL): token of each
+ *                                       row, -1 for rows >= rank_offset[R]
+ *   workspace     device, >= ep_rank_layout_workspace_bytes(cfg) bytes,
+ *                 256-byte aligned; scratch
+ * Deduplicated dispatch is ep_dispatch with rank_slot as its slot map: each
+ * token is written once per rank it needs (receive buffer of T*k rows, of
+ * which rank_offset[R] are used).  Deterministic. */
+EP_API size_t ep_rank_layout_workspace_bytes(const ep_config_t* cfg);
+EP_API int ep_get_rank_layout(const ep_config_t* cfg, const int32_t* topk_idx, int32_t* rank_count,
+                              int32_t* rank_offset, int32_t* rank_slot, int32_t* rank_token, void* workspace,
+                              size_t workspace_bytes, void* stream);
+
+/* In-rank partial combine: every rank sums its own experts' outputs for a
+ * token before one row goes back ([DAY2] "All-to-All通信": forward and
+ * accumulate).  For each first pick j on rank r of token t
+ * (rank_slot[t,j] = row): acc = +0; for j' = 0..k-1 in order with pick j'
+ * routed to rank r and slot[t,j'] in [0, T*k): acc = fma(topk_w[t,j'],
+ * y[slot[t,j'], c], acc); partial[row, c] = bf16_rne(acc).
+ *   y          device, bf16 [T*k, H] expert outputs in ep_get_layout's
+ *              receive rows, 16-byte aligned
+ *   topk_idx   device, int32 [T, k] (gives each pick's rank)
+ *   slot       device, int32 [T, k] from ep_get_layout
+ *   topk_w     device, fp32 [T, k]
+ *   rank_slot  device, int32 [T, k] from ep_get_rank_layout
+ *   partial    device, bf16 [T*k, H] out, 16-byte aligned; rows no
+ *              rank_slot names are not written */
+EP_API int ep_combine_rank_partial(const ep_config_t* cfg, const void* y, const int32_t* topk_idx,
+                                   const int32_t* slot, const float* topk_w, const int32_t* rank_slot,
+                                   void* partial, void* stream);
+
+/* Combine of the partial rows: out[t,c] = bf16_rne(((+0 + p_0) + p_1) + ...)
+ * over the token's partial rows p_i = partial[rank_slot[t,j]] for j
+ * ascending with rank_slot[t,j] in [0, T*k), in fp32.
+ *   partial    device, bf16 [T*k, H], 16-byte aligned
+ *   rank_slot  device, int32 [T, k]
+ *   out        device, bf16 [T, H], 16-byte aligned */
+EP_API int ep_combine_ranks(const ep_config_t* cfg, const void* partial, const int32_t* rank_slot, void* out,
+                            void* stream);
+
 /* CU budget ([GH#6] "Technical Overview of DeepEP": SM-count control; [DAY2]
  * "All-to-All通信": communication kernels confined to a few SMs and
  * overlapped with the compute stream).  Creates a HIP stream whose kernels

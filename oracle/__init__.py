@@ -61,6 +61,10 @@ def lib() -> ctypes.CDLL:
         L.orc_route.argtypes = [I, I, I, I, I, I, P, P, P]; L.orc_route.restype = I
         L.orc_layout.argtypes = [I, I, I, I, P, P, P, P, P, P]; L.orc_layout.restype = I
         L.orc_ll_layout.argtypes = [I, I, I, I, P, P, P, P]; L.orc_ll_layout.restype = I
+        L.orc_rank_layout.argtypes = [I, I, I, I, P, P, P, P, P]; L.orc_rank_layout.restype = I
+        L.orc_combine_rank_partial.argtypes = [I, I, I, I, I, I, P, P, P, P, P, I, P]
+        L.orc_combine_rank_partial.restype = None
+        L.orc_combine_ranks.argtypes = [I, I, I, I, P, P, P]; L.orc_combine_ranks.restype = None
         L.orc_dispatch_fp8.argtypes = [I, I, I, I, P, P, P, P]; L.orc_dispatch_fp8.restype = None
         L.orc_dispatch_bf16.argtypes = [I, I, I, I, P, P, P]; L.orc_dispatch_bf16.restype = None
         L.orc_combine.argtypes = [I, I, I, I, P, P, P, P]; L.orc_combine.restype = None
@@ -230,4 +234,48 @@ def combine_f64(y_bf16, slot, w) -> np.ndarray:
     T, k = slot.shape
     out = np.empty((T, H), np.float64)
     lib().orc_combine_f64(T, H, k, nrows, _p(y), _p(slot), _p(w), _p(out))
+    return out
+
+
+def rank_layout(topk_idx, E: int, R: int):
+    """Per-rank deduplicated layout: dict(rank_count [R], rank_offset [R+1],
+    rank_slot [T, k], rank_token [T*k])."""
+    idx = _c(topk_idx, np.int32)
+    T, k = idx.shape
+    cnt = np.empty(R, np.int32)
+    off = np.empty(R + 1, np.int32)
+    rslot = np.empty((T, k), np.int32)
+    rtok = np.empty(T * k, np.int32)
+    rc = lib().orc_rank_layout(T, k, E, R, _p(idx), _p(cnt), _p(off), _p(rslot), _p(rtok))
+    if rc != 0:
+        raise ValueError("invalid rank layout configuration")
+    return dict(rank_count=cnt, rank_offset=off, rank_slot=rslot, rank_token=rtok)
+
+
+def combine_rank_partial(y_bf16, topk_idx, slot, w, rank_slot, E: int, R: int, nrows_partial: int, partial=None):
+    """In-rank partial combine: uint16 partial rows [nrows_partial, H]; rows
+    no rank_slot names keep `partial`'s values (zero if not given)."""
+    y = _c(y_bf16, np.uint16)
+    idx = _c(topk_idx, np.int32)
+    slot = _c(slot, np.int32)
+    w = _c(w, np.float32)
+    rslot = _c(rank_slot, np.int32)
+    nrows, H = y.shape
+    T, k = idx.shape
+    if partial is None:
+        partial = np.zeros((nrows_partial, H), np.uint16)
+    partial = _c(partial, np.uint16)
+    lib().orc_combine_rank_partial(T, H, k, E, R, nrows, _p(y), _p(idx), _p(slot), _p(w), _p(rslot),
+                                   nrows_partial, _p(partial))
+    return partial
+
+
+def combine_ranks(partial_bf16, rank_slot) -> np.ndarray:
+    """Sum of each token's partial rows (first-pick order), rounded to bf16."""
+    p = _c(partial_bf16, np.uint16)
+    rslot = _c(rank_slot, np.int32)
+    nrows_partial, H = p.shape
+    T, k = rslot.shape
+    out = np.empty((T, H), np.uint16)
+    lib().orc_combine_ranks(T, H, k, nrows_partial, _p(p), _p(rslot), _p(out))
     return out

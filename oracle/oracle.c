@@ -367,3 +367,92 @@ void orc_combine_f64(int T, int H, int k, int nrows, const uint16_t* y,
             out[(long)t * H + c] = acc;
         }
 }
+
+/* ---------------------------------------------------------------------------
+ * Per-rank deduplication: a token travels once to each rank it needs, and a
+ * rank sums its own experts' outputs for the token before sending one row
+ * back ([DAY2] "DeepEP是什么", "All-to-All通信").
+ * ------------------------------------------------------------------------- */
+static int first_on_rank(const int32_t* picks, int j, int E, int EPR) {
+    int e = picks[j];
+    if (e < 0 || e >= E) return 0;
+    for (int jj = 0; jj < j; ++jj) {
+        int e2 = picks[jj];
+        if (e2 >= 0 && e2 < E && e2 / EPR == e / EPR) return 0;
+    }
+    return 1;
+}
+
+int orc_rank_layout(int T, int k, int E, int R, const int32_t* topk_idx,
+                    int32_t* rank_count, int32_t* rank_offset,
+                    int32_t* rank_slot, int32_t* rank_token) {
+    if (T < 0 || k < 1 || E < 1 || R < 1 || E % R != 0) return -1;
+    int EPR = E / R;
+    long P = (long)T * k;
+    for (int r = 0; r < R; ++r) rank_count[r] = 0;
+    for (int t = 0; t < T; ++t)
+        for (int j = 0; j < k; ++j)
+            if (first_on_rank(topk_idx + (long)t * k, j, E, EPR))
+                rank_count[topk_idx[(long)t * k + j] / EPR] += 1;
+    rank_offset[0] = 0;
+    for (int r = 0; r < R; ++r) rank_offset[r + 1] = rank_offset[r] + rank_count[r];
+    int32_t* fill = (int32_t*)calloc((size_t)R, sizeof(int32_t));
+    for (int t = 0; t < T; ++t)
+        for (int j = 0; j < k; ++j) {
+            long p = (long)t * k + j;
+            if (first_on_rank(topk_idx + (long)t * k, j, E, EPR)) {
+                int r = topk_idx[p] / EPR;
+                rank_slot[p] = rank_offset[r] + fill[r];
+                fill[r] += 1;
+            } else {
+                rank_slot[p] = -1;
+            }
+        }
+    free(fill);
+    if (rank_token) {
+        for (long row = 0; row < P; ++row) rank_token[row] = -1;
+        for (long p = 0; p < P; ++p)
+            if (rank_slot[p] >= 0) rank_token[rank_slot[p]] = (int32_t)(p / k);
+    }
+    return 0;
+}
+
+void orc_combine_rank_partial(int T, int H, int k, int E, int R, int nrows,
+                              const uint16_t* y, const int32_t* topk_idx,
+                              const int32_t* slot, const float* w,
+                              const int32_t* rank_slot, int nrows_partial,
+                              uint16_t* partial) {
+    int EPR = E / R;
+    for (int t = 0; t < T; ++t)
+        for (int j = 0; j < k; ++j) {
+            int row = rank_slot[(long)t * k + j];
+            if (row < 0 || row >= nrows_partial) continue;
+            int rank = topk_idx[(long)t * k + j] / EPR;
+            for (int c = 0; c < H; ++c) {
+                float acc = 0.0f;
+                for (int jj = 0; jj < k; ++jj) {
+                    int e = topk_idx[(long)t * k + jj];
+                    if (e < 0 || e >= E || e / EPR != rank) continue;
+                    int r = slot[(long)t * k + jj];
+                    if (r < 0 || r >= nrows) continue;
+                    acc = fmaf(w[(long)t * k + jj], orc_bf16_to_f32(y[(long)r * H + c]), acc);
+                }
+                partial[(long)row * H + c] = orc_bf16_from_f32(acc);
+            }
+        }
+}
+
+void orc_combine_ranks(int T, int H, int k, int nrows_partial,
+                       const uint16_t* partial, const int32_t* rank_slot,
+                       uint16_t* out) {
+    for (int t = 0; t < T; ++t)
+        for (int c = 0; c < H; ++c) {
+            float acc = 0.0f;
+            for (int j = 0; j < k; ++j) {
+                int row = rank_slot[(long)t * k + j];
+                if (row < 0 || row >= nrows_partial) continue;
+                acc = acc + orc_bf16_to_f32(partial[(long)row * H + c]);
+            }
+            out[(long)t * H + c] = orc_bf16_from_f32(acc);
+        }
+}

@@ -126,6 +126,45 @@ void orc_dispatch_bf16(int T, int H, int k, int nrows, const uint16_t* x,
 void orc_combine(int T, int H, int k, int nrows, const uint16_t* y,
                  const int32_t* slot, const float* w, uint16_t* out);
 
+/* Per-rank deduplicated layout ([DAY2] "DeepEP是什么" and "All-to-All通信":
+ * the normal kernels send a token once towards each destination and fan it
+ * out there, and accumulate expert outputs on the way back; the layout
+ * below is this library's reading for virtual ranks).  Rank r owns experts
+ * [r*E/R, (r+1)*E/R).  Pick j of token t is the token's first pick on its
+ * rank when no earlier pick j' < j of t is routed to an expert of the same
+ * rank.  One receive row per (token, rank) with a routed pick; rows grouped
+ * by rank, tokens ascending within a rank:
+ *   rank_count[r]    tokens with a routed pick on rank r                  (R)
+ *   rank_offset[r]   exclusive prefix sum of rank_count, [R] = total  (R + 1)
+ *   rank_slot[t,j]   the (t, rank) row when pick j is the token's first pick
+ *                    on its rank; -1 for later picks on the same rank and
+ *                    for unrouted picks                               (T x k)
+ *   rank_token[row]  token of each row, -1 for rows >= rank_offset[R]; may
+ *                    be NULL                                          (T * k)
+ * Returns 0, or -1 on an invalid configuration. */
+int orc_rank_layout(int T, int k, int E, int R, const int32_t* topk_idx,
+                    int32_t* rank_count, int32_t* rank_offset,
+                    int32_t* rank_slot, int32_t* rank_token);
+
+/* In-rank partial combine: for every pick j that is its token's first pick
+ * on rank r (rank_slot[t,j] = row in [0, nrows_partial)):
+ *   acc = 0; for j' = 0..k-1 with pick j' routed to rank r and
+ *       0 <= slot[t,j'] < nrows:  acc = fma(w[t,j'], y[slot[t,j'], c], acc)
+ *   partial[row, c] = bf16_rne(acc)
+ * Rows no rank_slot names are left untouched. */
+void orc_combine_rank_partial(int T, int H, int k, int E, int R, int nrows,
+                              const uint16_t* y, const int32_t* topk_idx,
+                              const int32_t* slot, const float* w,
+                              const int32_t* rank_slot, int nrows_partial,
+                              uint16_t* partial);
+
+/* Combine of the partial rows: out[t,c] = bf16_rne(((0 + p_0) + p_1) + ...)
+ * where p_0, p_1, ... are the token's partial rows partial[rank_slot[t,j]]
+ * for j ascending with 0 <= rank_slot[t,j] < nrows_partial. */
+void orc_combine_ranks(int T, int H, int k, int nrows_partial,
+                       const uint16_t* partial, const int32_t* rank_slot,
+                       uint16_t* out);
+
 /* Combine in fp64: out[t,c] = sum_j w[t,j] * y[slot[t,j], c], where each
  * product is exact in fp64 (24 + 8 significant bits) and the sum of k of
  * them is within k * 2^-53 * sum_j |w y| of the exact value.  Used to bound

@@ -165,6 +165,28 @@ def test_low_latency_rejections():
     assert lib.ep_combine_ll(ctypes.byref(z), 4, None, None, None, None, None) == L.EP_OK
 
 
+def test_rank_path_rejections():
+    lib = ep.lib()
+    c = _cfg().c()
+    need = lib.ep_rank_layout_workspace_bytes(ctypes.byref(c))
+    assert need > 0 and need % 256 == 0
+    assert lib.ep_rank_layout_workspace_bytes(ctypes.byref(_cfg(H=100).c())) == 0
+    a4 = [FAKE] * 4
+    assert lib.ep_get_rank_layout(ctypes.byref(c), *a4, FAKE, FAKE, need - 1, None) == L.EP_ERR_WORKSPACE
+    assert lib.ep_get_rank_layout(ctypes.byref(c), *a4, FAKE, None, need, None) == L.EP_ERR_WORKSPACE
+    assert lib.ep_get_rank_layout(ctypes.byref(c), *a4, FAKE, FAKE + 128, need, None) == L.EP_ERR_ALIGNMENT
+    assert lib.ep_get_rank_layout(ctypes.byref(c), FAKE, None, FAKE, FAKE, FAKE, FAKE, need,
+                                  None) == L.EP_ERR_INVALID_ARG
+    assert lib.ep_combine_rank_partial(ctypes.byref(c), FAKE, FAKE, FAKE, FAKE, FAKE, None,
+                                       None) == L.EP_ERR_INVALID_ARG
+    assert lib.ep_combine_rank_partial(ctypes.byref(c), FAKE + 8, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                       None) == L.EP_ERR_ALIGNMENT
+    assert lib.ep_combine_ranks(ctypes.byref(c), FAKE, FAKE, None, None) == L.EP_ERR_INVALID_ARG
+    assert lib.ep_combine_ranks(ctypes.byref(c), FAKE, FAKE + 2, FAKE, None) == L.EP_ERR_ALIGNMENT
+    z = _cfg(T=0).c()
+    assert lib.ep_combine_ranks(ctypes.byref(z), None, None, None, None) == L.EP_OK
+
+
 def test_cu_range_stream_rejections():
     lib = ep.lib()
     h = ctypes.c_void_p()
