@@ -9,7 +9,7 @@
 // code = e4m3_rne(x * inv).
 //
 // One-wave workgroups stride over the (token, 64-lane piece of its row)
-// items; a lane's piece is read once and written to the token's k receive
+// items (in XCD-contiguous order for large batches, launch.h); a lane's piece is read once and written to the token's k receive
 // rows (rows.h: 16 channels per lane for FP8, 8 for BF16).  Receive-row
 // indices are loaded once per wavefront and broadcast with v_readlane.
 //
@@ -27,10 +27,11 @@ __global__ __launch_bounds__(64, 8) void dispatch_fp8_kernel(const uint16_t* __r
                                                              const int32_t* __restrict__ slot,
                                                              uint8_t* __restrict__ recv,
                                                              float* __restrict__ recv_sc, int H, int k,
-                                                             int nrows, int segs, int items) {
+                                                             int nrows, int segs, int items, bool xcd_order) {
     const int lane = threadIdx.x;
     const int nchunks = H >> 4;
-    for (int item = blockIdx.x; item < items; item += gridDim.x) {
+    for (int v = blockIdx.x; v < items; v += gridDim.x) {
+        const int item = xcd_order ? xcd_item(v, items) : v;
         const int t = item / segs;
         const int chunk = (item - t * segs) * 64 + lane;  // 16-channel piece of row t
 
@@ -46,10 +47,11 @@ __global__ __launch_bounds__(64, 8) void dispatch_fp8_kernel(const uint16_t* __r
 __global__ __launch_bounds__(64, 8) void dispatch_bf16_kernel(const uint16_t* __restrict__ x,
                                                               const int32_t* __restrict__ slot,
                                                               uint16_t* __restrict__ recv, int H, int k,
-                                                              int nrows, int segs, int items) {
+                                                              int nrows, int segs, int items, bool xcd_order) {
     const int lane = threadIdx.x;
     const int nchunks = H >> 3;
-    for (int item = blockIdx.x; item < items; item += gridDim.x) {
+    for (int v = blockIdx.x; v < items; v += gridDim.x) {
+        const int item = xcd_order ? xcd_item(v, items) : v;
         const int t = item / segs;
         const int chunk = (item - t * segs) * 64 + lane;  // 8-channel piece of row t
 
@@ -67,7 +69,7 @@ hipError_t launch_dispatch_fp8(const Shape& s, const uint16_t* x, const int32_t*
     if (s.T == 0) return hipSuccess;
     const RowGrid g = row_grid(s.T, s.H >> 4);
     hipLaunchKernelGGL(dispatch_fp8_kernel, dim3(g.blocks), dim3(64), 0, stream, x, slot, recv, recv_scales,
-                       s.H, s.k, s.T * s.k, g.segs, g.items);
+                       s.H, s.k, s.T * s.k, g.segs, g.items, s.T >= kXcdOrderMinTokens);
     return hipGetLastError();
 }
 
@@ -76,7 +78,7 @@ hipError_t launch_dispatch_bf16(const Shape& s, const uint16_t* x, const int32_t
     if (s.T == 0) return hipSuccess;
     const RowGrid g = row_grid(s.T, s.H >> 3);
     hipLaunchKernelGGL(dispatch_bf16_kernel, dim3(g.blocks), dim3(64), 0, stream, x, slot, recv, s.H, s.k,
-                       s.T * s.k, g.segs, g.items);
+                       s.T * s.k, g.segs, g.items, s.T >= kXcdOrderMinTokens);
     return hipGetLastError();
 }
 
