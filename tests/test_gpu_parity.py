@@ -115,6 +115,12 @@ EDGE = {
     "k1_g1": W.Workload("k1", T=200, H=256, E=16, G=1, TG=1, k=1, R=16, seed=9),
     "tg1_m8": W.Workload("tg1", T=100, H=512, E=64, G=4, TG=1, k=16, R=2, m=8, seed=10),
     "e8_odd": W.Workload("e8", T=64, H=128, E=8, G=2, TG=2, k=3, R=1, seed=11),
+    # gate kernel branches: a 64-expert group (merge across the two half-waves),
+    # one-expert groups (no merge step), m = 1 with a group limit, E < 64
+    "gs64": W.Workload("gs64", T=300, H=256, E=256, G=4, TG=2, k=8, R=8, m=2, seed=13),
+    "gs1": W.Workload("gs1", T=300, H=256, E=16, G=16, TG=5, k=4, R=4, seed=14),
+    "m1_tg3": W.Workload("m1", T=300, H=256, E=64, G=8, TG=3, k=6, R=8, m=1, seed=15),
+    "e32_gs8": W.Workload("e32", T=129, H=128, E=32, G=4, TG=3, k=5, R=2, seed=16),
 }
 
 
