@@ -25,6 +25,8 @@ namespace ep {
 namespace {
 
 constexpr int kMaxBlockThreads = 1024;
+// row pieces per thread: H/16 <= 1024 FP8 pieces, H/8 <= 2048 BF16 pieces
+constexpr int kLLPieces = 2;
 
 template <bool FP8>
 __global__ __launch_bounds__(kMaxBlockThreads) void dispatch_ll_kernel(
@@ -51,6 +53,22 @@ __global__ __launch_bounds__(kMaxBlockThreads) void dispatch_ll_kernel(
     }
 
     const int t = blockIdx.x;
+    const uint16_t* xrow = x + (size_t)t * H;
+    // the token's row pieces do not depend on the positions: load them first
+    // so their latency overlaps the position count (a thread owns at most
+    // kLLPieces pieces: blockDim covers H/16 FP8 pieces, or half the H/8 BF16
+    // pieces at H = 16384)
+    const int npieces = FP8 ? (H >> 4) : (H >> 3);
+    Fp8Piece pf[kLLPieces];
+    i32x4 pb[kLLPieces];
+#pragma unroll
+    for (int u = 0; u < kLLPieces; ++u) {
+        const int chunk = tid + u * (int)blockDim.x;
+        if (chunk < npieces) {
+            if (FP8) pf[u] = fp8_load(xrow, chunk, H);
+            else pb[u] = bf16_load(xrow, chunk, H);
+        }
+    }
     if (tid < kMaxTopkLL) s_cnt[tid] = 0;
     int my_e = -1;  // lane j < k: expert of pick j, -1 if unrouted
     if (lane < k) {
@@ -94,14 +112,14 @@ __global__ __launch_bounds__(kMaxBlockThreads) void dispatch_ll_kernel(
     }
 
     const int nrows = E * cap;
-    const uint16_t* xrow = x + (size_t)t * H;
-    if (FP8) {
-        // 8-lane scale blocks stay together: H/16 and blockDim are multiples of 8
-        for (int chunk = tid; chunk < (H >> 4); chunk += blockDim.x)
-            fp8_piece(xrow, chunk, H, k, my_slot, nrows, static_cast<uint8_t*>(recv), recv_sc);
-    } else {
-        for (int chunk = tid; chunk < (H >> 3); chunk += blockDim.x)
-            bf16_piece(xrow, chunk, H, k, my_slot, nrows, static_cast<uint16_t*>(recv));
+    // 8-lane scale blocks stay together: H/16 and blockDim are multiples of 8
+#pragma unroll
+    for (int u = 0; u < kLLPieces; ++u) {
+        const int chunk = tid + u * (int)blockDim.x;
+        if (chunk < npieces) {
+            if (FP8) fp8_store(pf[u], chunk, H, k, my_slot, nrows, static_cast<uint8_t*>(recv), recv_sc);
+            else bf16_store(pb[u], chunk, H, k, my_slot, nrows, static_cast<uint16_t*>(recv));
+        }
     }
 }
 

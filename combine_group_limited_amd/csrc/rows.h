@@ -12,17 +12,27 @@ namespace ep {
 
 // FP8: a lane owns 16 consecutive channels (`chunk` counts 16-channel
 // pieces), so a 128-channel scale block is 8 adjacent lanes and its amax a
-// 3-step butterfly.  All 8 lanes of a block must call this together.
+// 3-step butterfly.  All 8 lanes of a block must store together.
 // Per block: a = max(amax, 1e-4), inv = 448 / a, scale = a / 448,
 // code = e4m3_rne(x * inv).  x is read with default caching, the codes are
-// streamed (nt).
-__device__ __forceinline__ void fp8_piece(const uint16_t* __restrict__ xrow, int chunk, int H, int k,
-                                          int my_slot, int nrows, uint8_t* __restrict__ recv,
-                                          float* __restrict__ recv_sc) {
-    const int lane = threadIdx.x & 63;
+// streamed (nt).  Loading and storing are separate steps so that a caller
+// can issue the loads before work the stores depend on.
+struct Fp8Piece {
+    i32x4 a, b;
+};
+
+__device__ __forceinline__ Fp8Piece fp8_load(const uint16_t* __restrict__ xrow, int chunk, int H) {
     const auto xr = buffer_rsrc(xrow, (uint32_t)H * 2u);
-    const i32x4 a = __builtin_amdgcn_raw_buffer_load_b128(xr, chunk * 32, 0, kCached);
-    const i32x4 b = __builtin_amdgcn_raw_buffer_load_b128(xr, chunk * 32 + 16, 0, kCached);
+    Fp8Piece v;
+    v.a = __builtin_amdgcn_raw_buffer_load_b128(xr, chunk * 32, 0, kCached);
+    v.b = __builtin_amdgcn_raw_buffer_load_b128(xr, chunk * 32 + 16, 0, kCached);
+    return v;
+}
+
+__device__ __forceinline__ void fp8_store(const Fp8Piece& v, int chunk, int H, int k, int my_slot, int nrows,
+                                          uint8_t* __restrict__ recv, float* __restrict__ recv_sc) {
+    const int lane = threadIdx.x & 63;
+    const i32x4 a = v.a, b = v.b;
     float f[16];
     f[0] = bf16_lo(a.x);  f[1] = bf16_hi(a.x);  f[2] = bf16_lo(a.y);  f[3] = bf16_hi(a.y);
     f[4] = bf16_lo(a.z);  f[5] = bf16_hi(a.z);  f[6] = bf16_lo(a.w);  f[7] = bf16_hi(a.w);
@@ -56,12 +66,20 @@ __device__ __forceinline__ void fp8_piece(const uint16_t* __restrict__ xrow, int
     }
 }
 
+__device__ __forceinline__ void fp8_piece(const uint16_t* __restrict__ xrow, int chunk, int H, int k,
+                                          int my_slot, int nrows, uint8_t* __restrict__ recv,
+                                          float* __restrict__ recv_sc) {
+    fp8_store(fp8_load(xrow, chunk, H), chunk, H, k, my_slot, nrows, recv, recv_sc);
+}
+
 // BF16: a lane owns 8 channels (`chunk` counts 8-channel pieces): one 16-byte
 // load, one 16-byte streamed store per receive row.
-__device__ __forceinline__ void bf16_piece(const uint16_t* __restrict__ xrow, int chunk, int H, int k,
-                                           int my_slot, int nrows, uint16_t* __restrict__ recv) {
-    const auto xr = buffer_rsrc(xrow, (uint32_t)H * 2u);
-    const i32x4 v = __builtin_amdgcn_raw_buffer_load_b128(xr, chunk * 16, 0, kCached);
+__device__ __forceinline__ i32x4 bf16_load(const uint16_t* __restrict__ xrow, int chunk, int H) {
+    return __builtin_amdgcn_raw_buffer_load_b128(buffer_rsrc(xrow, (uint32_t)H * 2u), chunk * 16, 0, kCached);
+}
+
+__device__ __forceinline__ void bf16_store(i32x4 v, int chunk, int H, int k, int my_slot, int nrows,
+                                           uint16_t* __restrict__ recv) {
     for (int j = 0; j < k; ++j) {
         const int r = __builtin_amdgcn_readlane(my_slot, j);
         if ((unsigned)r < (unsigned)nrows) {
@@ -69,6 +87,11 @@ __device__ __forceinline__ void bf16_piece(const uint16_t* __restrict__ xrow, in
             __builtin_amdgcn_raw_buffer_store_b128(v, rr, chunk * 16, 0, kStream);
         }
     }
+}
+
+__device__ __forceinline__ void bf16_piece(const uint16_t* __restrict__ xrow, int chunk, int H, int k,
+                                           int my_slot, int nrows, uint16_t* __restrict__ recv) {
+    bf16_store(bf16_load(xrow, chunk, H), chunk, H, k, my_slot, nrows, recv);
 }
 
 }  // namespace ep
