@@ -10,7 +10,9 @@ are a resident synthetic buffer (the expert computation is not part of the
 path).
 
 Every buffer exists in several copies used round-robin, so that each step
-reads its inputs from HBM rather than from the 256 MB Infinity Cache.
+reads its inputs from HBM rather than from the 256 MB Infinity Cache.  The
+line also reports the step replayed from a captured HIP graph
+(`graph_step_us`), which removes the host's launch gaps.
 
 Prints one JSON line.  `value` is dispatch+combine algorithmic bytes divided
 by the summed average durations of the dispatch and combine kernels, from
@@ -177,6 +179,47 @@ def timed_steps(args, nsets, launch_stages, stages):
     return dur, wall
 
 
+def launch_step(lib, cp, p, code, ws, nws, sh, check):
+    """One step of the normal path on stream handle `sh`, no events."""
+    check(lib.ep_route(cp, p["logits"], p["idx"], p["wt"], sh), "ep_route")
+    check(lib.ep_get_layout(cp, p["idx"], p["cnt"], p["ntok"], p["off"], p["slot"], p["recv_token"],
+                            ws.data_ptr(), nws, sh), "ep_get_layout")
+    check(lib.ep_dispatch(cp, p["x"], p["slot"], code, p["recv"], p["scales"], sh), "ep_dispatch")
+    check(lib.ep_combine(cp, p["y"], p["slot"], p["wt"], p["out"], sh), "ep_combine")
+
+
+def graph_step_us(args, nsets, step_on):
+    """Average time of one step replayed from a captured HIP graph (one graph
+    per buffer set, used round-robin), events around all replays."""
+    import torch
+    graphs = []
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step_on(0, side.cuda_stream)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    for i in range(nsets):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            step_on(i, torch.cuda.current_stream().cuda_stream)
+        graphs.append(g)
+    for i in range(max(args.warmup, 1)):
+        graphs[i % nsets].replay()
+    torch.cuda.synchronize()
+    hev = HipEvents()
+    e = hev.create(2)
+    sh = int(torch.cuda.current_stream().cuda_stream)
+    hev.record(e[0], sh)
+    for i in range(args.steps):
+        graphs[i % nsets].replay()
+    hev.record(e[1], sh)
+    t = hev.seconds(e[0], e[1]) / args.steps
+    hev.destroy(e)
+    del graphs
+    return t * 1e6
+
+
 def kernel_table(dur, bytes_):
     import numpy as np
     out = {}
@@ -263,6 +306,7 @@ def run_normal(args, w):
     stages = ("route", "layout", "dispatch", "combine")
     dur, wall = timed_steps(args, nsets, launch, stages)
     kt = kernel_table(dur, bytes_)
+    graph_us = graph_step_us(args, nsets, lambda i, sh: launch_step(lib, cp, ptr[i], code, ws, nws, sh, check))
     avg = {s: kt[s]["avg_us"] * 1e-6 for s in stages}
     dc_bytes = bytes_["dispatch"] + bytes_["combine"]
     dc_time = avg["dispatch"] + avg["combine"]
@@ -292,6 +336,8 @@ def run_normal(args, w):
         "dispatch_combine_us": round(dc_time * 1e6, 2),
         "tokens_per_s": round(w.T / dc_time, 1),
         "step_tokens_per_s": round(w.T / (wall / args.steps), 1),
+        "graph_step_us": round(graph_us, 2),
+        "graph_step_tokens_per_s": round(w.T / (graph_us * 1e-6), 1),
         "roofline": {"kernel": "combine", "bound": "hbm", "achieved": round(comb_gbs, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(comb_gbs / HBM_PEAK_GBS, 4),
                      "traffic": _recorded_traffic("combine", w.name)},
