@@ -577,15 +577,17 @@ def run_dedup(args, w):
     import combine_group_limited_amd as ep
     from combine_group_limited_amd import _lib as L
     import workloads as W
-    import oracle  # only to count the rank rows of the seeded routing for the byte model
 
     cfg = ep.Config.of(w)
     dev = torch.device("cuda", 0)
     lg_np, x_np, y_np = W.gen_logits(w), W.gen_x(w), W.gen_y(w)
-    idx_np, _ = oracle.route(lg_np, w.G, w.TG, w.k, w.topm)
-    rows = int(oracle.rank_layout(idx_np, w.E, w.R)["rank_offset"][-1])
     B = w.H // 128
     P = w.T * w.k
+    logits0 = torch.from_numpy(lg_np).to(dev)
+    # rank rows of the seeded routing (the byte model depends on them), from
+    # the library's own rank layout
+    c_idx, _ = ep.route(cfg, logits0)
+    rows = int(ep.get_rank_layout(cfg, c_idx, with_rank_token=False)["rank_offset"][-1].item())
     bytes_ = dict(route=w.bytes_route(), layout=w.bytes_layout(),
                   rank_layout=P * 8 + 4 * (2 * w.R + 1),
                   dispatch=w.T * 2 * w.H + rows * (w.H + 4 * B) + 4 * P,
@@ -593,7 +595,6 @@ def run_dedup(args, w):
                   combine_ranks=2 * w.H * rows + 2 * w.H * w.T + 4 * P)
     touched = sum(bytes_.values())
     nsets = buffer_sets(args.sets, touched, touched)
-    logits0 = torch.from_numpy(lg_np).to(dev)
     x0 = torch.from_numpy(x_np.view(np.int16)).view(torch.bfloat16).to(dev)
     y0 = torch.from_numpy(y_np.view(np.int16)).view(torch.bfloat16).to(dev)
     i32 = dict(dtype=torch.int32, device=dev)
