@@ -12,9 +12,9 @@
 // the same expert -- the same in-expert order as the normal layout -- and
 // is dropped (slot -1) when pos >= cap.
 //
-// One workgroup per token: its waves share the count of earlier pairs per
-// pick (ballots over 64 entries at a time, summed in LDS), then store the
-// token's row pieces as the normal dispatch does (rows.h).  One extra
+// One workgroup per token: it counts the earlier routed pairs per expert in
+// an LDS histogram, then stores the token's row pieces as the normal
+// dispatch does (rows.h).  One extra
 // workgroup writes the per-expert counts.  The work to find positions grows
 // with T * k, so the path is limited to small batches (decode).
 #include "launch.h"
@@ -53,53 +53,49 @@ __global__ __launch_bounds__(kMaxBlockThreads) void dispatch_ll_kernel(
     }
 
     const int t = blockIdx.x;
+    // position of pick j = routed pairs of earlier tokens with the same
+    // expert (the entries [0, t*k) of idx), counted as a histogram over
+    // experts in LDS.  The first pass's entries (four per thread) and the
+    // token's own picks are loaded before the row pieces: loads complete in
+    // issue order, so waiting for these small cache-resident reads does not
+    // wait for the row pieces from HBM.  The loads are unconditional buffer
+    // loads (out of range ones return 0 and are masked afterwards) so the
+    // compiler can count what is still in flight.
+    const int before = t * k;
+    const int nt = blockDim.x;
+    const auto er = buffer_rsrc(idx, (uint32_t)before * 4u);
+    int v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) v[u] = (int)__builtin_amdgcn_raw_buffer_load_b32(er, (tid + u * nt) * 4, 0, kCached);
+    // lane j < k: expert of pick j, -1 if unrouted
+    int my_e = (int)__builtin_amdgcn_raw_buffer_load_b32(buffer_rsrc(idx + (size_t)before, (uint32_t)k * 4u),
+                                                          lane * 4, 0, kCached);
+
     const uint16_t* xrow = x + (size_t)t * H;
-    // the token's row pieces do not depend on the positions: load them first
-    // so their latency overlaps the position count (a thread owns at most
-    // kLLPieces pieces: blockDim covers H/16 FP8 pieces, or half the H/8 BF16
-    // pieces at H = 16384)
-    const int npieces = FP8 ? (H >> 4) : (H >> 3);
+    // the token's row pieces do not depend on the positions: load them now
+    // so their latency overlaps the count (a thread owns at most kLLPieces
+    // pieces: blockDim covers H/16 FP8 pieces, or half the H/8 BF16 pieces at
+    // H = 16384)
     Fp8Piece pf[kLLPieces];
     i32x4 pb[kLLPieces];
 #pragma unroll
     for (int u = 0; u < kLLPieces; ++u) {
-        const int chunk = tid + u * (int)blockDim.x;
-        if (chunk < npieces) {
-            if (FP8) pf[u] = fp8_load(xrow, chunk, H);
-            else pb[u] = bf16_load(xrow, chunk, H);
-        }
+        const int chunk = tid + u * nt;  // past the row: reads 0, never stored
+        if (FP8) pf[u] = fp8_load(xrow, chunk, H);
+        else pb[u] = bf16_load(xrow, chunk, H);
     }
-    if (tid < kMaxTopkLL) s_cnt[tid] = 0;
-    int my_e = -1;  // lane j < k: expert of pick j, -1 if unrouted
-    if (lane < k) {
-        const int v = idx[(size_t)t * k + lane];
-        my_e = (unsigned)v < (unsigned)E ? v : -1;
+    for (int i = tid; i < E; i += nt) s_cnt[i] = 0;
+    my_e = (lane < k && (unsigned)my_e < (unsigned)E) ? my_e : -1;
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+        if (tid + u * nt < before && (unsigned)v[u] < (unsigned)E) atomicAdd(&s_cnt[v[u]], 1);
+    for (int p = tid + 4 * nt; p < before; p += nt) {
+        const int e = idx[p];
+        if ((unsigned)e < (unsigned)E) atomicAdd(&s_cnt[e], 1);
     }
     __syncthreads();
-
-    // routed pairs of earlier tokens with the same expert, per pick: the
-    // entries [0, t*k) in chunks of 64, four chunks per wave in flight
-    const int before = t * k;
-    int part = 0;
-    for (int c0 = wave * 4; c0 * 64 < before; c0 += nw * 4) {
-        int v[4];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const int p = (c0 + u) * 64 + lane;
-            v[u] = p < before ? idx[p] : -1;
-        }
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            for (int j = 0; j < k; ++j) {
-                const int ej = __builtin_amdgcn_readlane(my_e, j);
-                const uint64_t m = __ballot(ej >= 0 && v[u] == ej);
-                part += (lane == j) ? __popcll(m) : 0;
-            }
-        }
-    }
-    if (lane < k && part > 0) atomicAdd(&s_cnt[lane], part);
-    __syncthreads();
-    int my_pos = lane < k ? s_cnt[lane] : 0;
+    int my_pos = my_e >= 0 ? s_cnt[my_e] : 0;
     // earlier picks of this token with the same expert (a repeated expert)
     for (int j = 0; j + 1 < k; ++j) {
         const int ej = __builtin_amdgcn_readlane(my_e, j);
@@ -112,6 +108,7 @@ __global__ __launch_bounds__(kMaxBlockThreads) void dispatch_ll_kernel(
     }
 
     const int nrows = E * cap;
+    const int npieces = FP8 ? (H >> 4) : (H >> 3);
     // 8-lane scale blocks stay together: H/16 and blockDim are multiples of 8
 #pragma unroll
     for (int u = 0; u < kLLPieces; ++u) {
