@@ -19,7 +19,9 @@
 //                          the lanes before it
 // Workspace: hist [E][C] and rank counts [R][C], int32, C = ceil(T*k / P)
 // with P = 64 * waves-per-block pairs per block.  Up to 64 count blocks the
-// scan folds into the assign launch (layout_assign_scan_kernel).
+// scan folds into the assign launch (layout_assign_scan_kernel); up to
+// kSmallMaxPairs pairs one workgroup does all three steps in one launch
+// (layout_small_kernel) and the workspace is not used.
 #include "device.h"
 #include "launch.h"
 
@@ -42,6 +44,13 @@ inline int layout_blocks(long P, int W) { return (int)((P + 64 * W - 1) / (64 * 
 // separate scan.
 constexpr int kSelfScanMaxBlocks = 64;
 
+// pairs up to which one workgroup does the whole layout in one launch.
+// Measured per call on MI355X, 256 experts, top-8: 256 pairs 8.6 -> 5.7 us,
+// 1024 pairs 8.0 -> 6.9 us; at 2048 pairs one workgroup is slower (9.0
+// against 8.2 us).
+constexpr long kSmallMaxPairs = 1024;
+constexpr size_t kSmallMaxLds = 65536;
+
 // exclusive block-wide prefix sum; `wsum` is LDS scratch of blockDim/64 ints
 __device__ int block_exclusive_sum(int v, int* total, int* wsum) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
@@ -57,6 +66,25 @@ __device__ int block_exclusive_sum(int v, int* total, int* wsum) {
     __syncthreads();
     *total = tot;
     return pre + inc - v;
+}
+
+// Whether pick j of a token (expert ids at row[0..k)) is the token's first
+// routed pick on the rank whose experts are [lo, lo + EPR): no earlier pick
+// lies in that range (an unrouted id, negative or >= E, never does).  The
+// earlier picks are read eight at a time with unconditional loads (indices
+// clamped into the row, extra reads unused), so all eight are in flight
+// together.
+__device__ __forceinline__ bool first_on_rank(const int32_t* __restrict__ row, int j, int lo, int EPR) {
+    bool first = true;
+    for (int j0 = 0; j0 < j; j0 += 8) {
+        int v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] = row[min(j0 + u, j - 1)];
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+            if (j0 + u < j && (unsigned)(v[u] - lo) < (unsigned)EPR) first = false;
+    }
+    return first;
 }
 
 __global__ __launch_bounds__(512) void layout_count_kernel(const int32_t* __restrict__ idx,
@@ -75,13 +103,7 @@ __global__ __launch_bounds__(512) void layout_count_kernel(const int32_t* __rest
             // a token counts once per rank: only its first pair on the rank adds
             const int r = e / EPR;
             const long t = p / k;
-            const int j = (int)(p - t * k);
-            bool first = true;
-            for (int jj = 0; jj < j; ++jj) {
-                const int e2 = idx[t * k + jj];
-                if ((unsigned)e2 < (unsigned)E && e2 / EPR == r) first = false;
-            }
-            if (first) atomicAdd(&cnt_sm[E + r], 1);
+            if (first_on_rank(idx + t * k, (int)(p - t * k), r * EPR, EPR)) atomicAdd(&cnt_sm[E + r], 1);
         }
     }
     __syncthreads();
@@ -271,6 +293,93 @@ __global__ __launch_bounds__(W * 64) void layout_assign_scan_kernel(
     assign_block<W>(idx, base, mask, wpre, slot, recv_token, P, k, E, total, c);
 }
 
+// Small inputs in one launch and one workgroup: the P expert ids are
+// staged in LDS once; LDS histograms of experts and of first-on-rank pairs,
+// a block-wide scan into the expert offsets, then the pairs in chunks of
+// W*64 in order, each chunk ranked as in assign_block while `base` carries
+// every expert's next row from chunk to chunk.  For P up to kSmallMaxPairs,
+// where one workgroup beats two launches.
+template <int W>
+__global__ __launch_bounds__(W * 64) void layout_small_kernel(
+    const int32_t* __restrict__ idx, int32_t* __restrict__ cnt, int32_t* __restrict__ ntok_rank,
+    int32_t* __restrict__ off, int32_t* __restrict__ slot, int32_t* __restrict__ recv_token, long P, int k,
+    int E, int R, int EPR) {
+    extern __shared__ __align__(16) unsigned char sm_sm[];
+    uint64_t* mask = reinterpret_cast<uint64_t*>(sm_sm);        // [W][E]
+    int32_t* wpre = reinterpret_cast<int32_t*>(mask + W * E);    // [W][E]
+    int32_t* base = wpre + W * E;                                // [E]
+    int32_t* ids = base + E;                                     // [P] expert ids, -1 if unrouted
+    int32_t* tot = wpre;                                         // [E] counts, then [R] rank counts; in wpre
+    int32_t* rtot = wpre + E;                                    //   until the first chunk is ranked
+    __shared__ int wsum[W];
+
+    const int tid = threadIdx.x;
+    constexpr int NT = W * 64;
+    // eight unconditional buffer loads in flight per thread (out of range
+    // ones read 0 and are not kept), so staging waits about once per 8*NT
+    // pairs instead of once per NT
+    const auto ir = buffer_rsrc(idx, (uint32_t)P * 4u);
+    for (int p0 = tid; p0 < P; p0 += 8 * NT) {
+        int v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] = (int)__builtin_amdgcn_raw_buffer_load_b32(ir, (p0 + u * NT) * 4, 0, kCached);
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int p = p0 + u * NT;
+            if (p < P) ids[p] = (unsigned)v[u] < (unsigned)E ? v[u] : -1;
+        }
+    }
+    for (int i = tid; i < W * E; i += NT) mask[i] = 0ull;
+    for (int i = tid; i < E + R; i += NT) tot[i] = 0;
+    __syncthreads();
+    for (int p = tid; p < P; p += NT) {
+        const int e = ids[p];
+        if (e >= 0) {
+            atomicAdd(&tot[e], 1);
+            // a token counts once per rank: only its first pair on the rank
+            // adds (an earlier pick in [lo, lo + EPR); unrouted ids are -1)
+            const int r = e / EPR;
+            const int lo = r * EPR;
+            const int t = p / k;
+            bool first = true;
+            for (int q = t * k; q < p; ++q)
+                if ((unsigned)(ids[q] - lo) < (unsigned)EPR) first = false;
+            if (first) atomicAdd(&rtot[r], 1);
+        }
+    }
+    __syncthreads();
+    for (int r = tid; r < R; r += NT) ntok_rank[r] = rtot[r];
+
+    // expert offsets: each thread scans EPT consecutive experts
+    const int EPT = (E + NT - 1) / NT;
+    const int e0 = tid * EPT;
+    int local = 0;
+    for (int i = 0; i < EPT; ++i)
+        if (e0 + i < E) local += tot[e0 + i];
+    int total;
+    int ex = block_exclusive_sum(local, &total, wsum);
+    for (int i = 0; i < EPT; ++i) {
+        const int e = e0 + i;
+        if (e < E) {
+            base[e] = ex;
+            off[e] = ex;
+            cnt[e] = tot[e];
+            ex += tot[e];
+        }
+    }
+    if (tid == 0) off[E] = total;
+    const int C = (int)((P + NT - 1) / NT);
+    for (int c = 0; c < C; ++c) {
+        assign_block<W>(ids, base, mask, wpre, slot, recv_token, P, k, E, total, c);
+        __syncthreads();
+        // the next chunk's rows start after this chunk's pairs
+        for (int i = tid; i < E; i += NT) {
+            base[i] += wpre[(W - 1) * E + i] + __popcll(mask[(W - 1) * E + i]);
+            for (int w = 0; w < W; ++w) mask[w * E + i] = 0ull;
+        }
+    }
+}
+
 template <int W>
 hipError_t launch_assign(const Shape& s, long P, int C, const int32_t* idx, const int32_t* hist,
                          const int32_t* cnt, int32_t* off, int32_t* slot, int32_t* recv_token,
@@ -294,13 +403,7 @@ __global__ __launch_bounds__(256) void rank_first_kernel(const int32_t* __restri
     if ((unsigned)e < (unsigned)E) {
         const int r = e / EPR;
         const long t = p / k;
-        const int j = (int)(p - t * k);
-        bool first = true;
-        for (int jj = 0; jj < j; ++jj) {
-            const int e2 = idx[t * k + jj];
-            if ((unsigned)e2 < (unsigned)E && e2 / EPR == r) first = false;
-        }
-        if (first) out = r;
+        if (first_on_rank(idx + t * k, (int)(p - t * k), r * EPR, EPR)) out = r;
     }
     ridx[p] = out;
 }
@@ -330,6 +433,17 @@ hipError_t launch_layout(const Shape& s, const int32_t* topk_idx, int32_t* cnt, 
     const int C = layout_blocks(P, W);
     int32_t* hist = static_cast<int32_t*>(ws);
     int32_t* rk = hist + (size_t)s.E * C;
+    const size_t small_lds = (size_t)(12 * W + 4) * s.E + (size_t)P * sizeof(int32_t);
+    if (P <= kSmallMaxPairs && small_lds <= kSmallMaxLds) {
+        const size_t lds = small_lds;
+        if (W == 8)
+            hipLaunchKernelGGL(layout_small_kernel<8>, dim3(1), dim3(8 * 64), lds, stream, topk_idx, cnt, ntok_rank,
+                               off, slot, recv_token, P, s.k, s.E, s.R, s.E / s.R);
+        else
+            hipLaunchKernelGGL(layout_small_kernel<4>, dim3(1), dim3(4 * 64), lds, stream, topk_idx, cnt, ntok_rank,
+                               off, slot, recv_token, P, s.k, s.E, s.R, s.E / s.R);
+        return hipGetLastError();
+    }
     if (C > 0) {
         hipLaunchKernelGGL(layout_count_kernel, dim3(C), dim3(W * 64), (size_t)(s.E + s.R) * sizeof(int32_t),
                            stream, topk_idx, hist, rk, P, s.k, s.E, s.R, s.E / s.R, C);

@@ -176,6 +176,31 @@ def test_unrouted_and_repeated_entries():
     assert_combine(to_host(out), oracle.combine(y, ol["slot"], wt))
 
 
+@pytest.mark.parametrize("T,E,k,R", [
+    (127, 256, 8, 32), (128, 256, 8, 32), (129, 256, 8, 32),   # one workgroup up to 1024 pairs, launches above
+    (128, 1024, 8, 64), (32, 1024, 32, 64), (33, 1024, 32, 64),  # four-wave workgroups (E = 1024), k = 32
+    (1, 256, 8, 32), (170, 48, 6, 8),
+])
+def test_layout_around_one_workgroup_limit(T, E, k, R):
+    # layout and rank layout of a hand-made topk_idx (unrouted -1 and >= E
+    # entries, repeated experts) on both sides of the one-workgroup size
+    w = W.Workload("lim", T=T, H=128, E=E, G=4, TG=4, k=k, R=R, seed=T * 7 + k)
+    say("layout limit", w)
+    rng = np.random.default_rng(w.seed)
+    idx = rng.integers(0, E, size=(T, k)).astype(np.int32)
+    idx[rng.random(idx.shape) < 0.08] = -1
+    idx[rng.random(idx.shape) < 0.02] = E + 3
+    cfg = ep.Config.of(w)
+    lay = ep.get_layout(cfg, to_dev(idx))
+    rl = ep.get_rank_layout(cfg, to_dev(idx))
+    ol = oracle.layout(idx, E, R)
+    orl = oracle.rank_layout(idx, E, R)
+    for key in ("cnt", "off", "ntok_rank", "slot", "recv_token"):
+        assert_same(key, to_host(lay[key]), ol[key])
+    for key in ("rank_count", "rank_offset", "rank_slot", "rank_token"):
+        assert_same(key, to_host(rl[key]), orl[key])
+
+
 def test_fp8_cast_covers_every_bf16_value():
     # blocks whose largest magnitude is A and whose other 127 values sweep
     # every bf16 pattern with |v| <= A; inv = 448 / max(A, 1e-4) takes
