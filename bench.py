@@ -226,6 +226,8 @@ def kernel_table(dur, bytes_):
     for s, v in dur.items():
         avg = float(np.mean(v))
         out[s] = {"avg_us": round(avg * 1e6, 4), "median_us": round(float(np.median(v)) * 1e6, 4),
+                  "p10_us": round(float(np.percentile(v, 10)) * 1e6, 4),
+                  "p90_us": round(float(np.percentile(v, 90)) * 1e6, 4),
                   "algorithmic_bytes": bytes_[s], "gbs": round(bytes_[s] / avg / 1e9, 4),
                   "frac": round(bytes_[s] / avg / 1e9 / HBM_PEAK_GBS, 4)}
     return out
