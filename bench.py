@@ -11,8 +11,9 @@ path).
 
 Every buffer exists in several copies used round-robin, so that each step
 reads its inputs from HBM rather than from the 256 MB Infinity Cache.  The
-line also reports the step replayed from a captured HIP graph
-(`graph_step_us`), which removes the host's launch gaps.
+line also reports the step replayed from a captured HIP graph that holds
+one step per buffer set (`graph_step_us`), which removes the host's launch
+gaps.
 
 Prints one JSON line.  `value` is dispatch+combine algorithmic bytes divided
 by the summed average durations of the dispatch and combine kernels, from
@@ -189,34 +190,34 @@ def launch_step(lib, cp, p, code, ws, nws, sh, check):
 
 
 def graph_step_us(args, nsets, step_on):
-    """Average time of one step replayed from a captured HIP graph (one graph
-    per buffer set, used round-robin), events around all replays."""
+    """Average time of one step replayed from a captured HIP graph.  One
+    graph holds one step per buffer set, in order, so a replay runs `nsets`
+    steps back to back and the graph's own launch cost is spread over them,
+    as when a loop of steps is captured; events around all replays."""
     import torch
-    graphs = []
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):
         step_on(0, side.cuda_stream)
     torch.cuda.current_stream().wait_stream(side)
     torch.cuda.synchronize()
-    for i in range(nsets):
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(nsets):
             step_on(i, torch.cuda.current_stream().cuda_stream)
-        graphs.append(g)
-    for i in range(max(args.warmup, 1)):
-        graphs[i % nsets].replay()
+    g.replay()
     torch.cuda.synchronize()
+    reps = max(1, -(-max(args.steps, 1) // nsets))
     hev = HipEvents()
     e = hev.create(2)
     sh = int(torch.cuda.current_stream().cuda_stream)
     hev.record(e[0], sh)
-    for i in range(args.steps):
-        graphs[i % nsets].replay()
+    for _ in range(reps):
+        g.replay()
     hev.record(e[1], sh)
-    t = hev.seconds(e[0], e[1]) / args.steps
+    t = hev.seconds(e[0], e[1]) / (reps * nsets)
     hev.destroy(e)
-    del graphs
+    del g
     return t * 1e6
 
 
@@ -408,19 +409,20 @@ def run_ll(args, w):
         if rc != 0:
             raise RuntimeError("%s failed: %s" % (name, lib.ep_strerror(rc).decode()))
 
-    def launch(i, rec):
+    def launch(i, rec, st=sh):
         p = ptr[i]
         rec(0)
-        check(lib.ep_route(cp, p["logits"], p["idx"], p["wt"], sh), "ep_route")
+        check(lib.ep_route(cp, p["logits"], p["idx"], p["wt"], st), "ep_route")
         rec(1)
         check(lib.ep_dispatch_ll(cp, p["x"], p["idx"], cap, code, p["recv"], p["scales"], p["count"], p["src"],
-                                 p["slot"], sh), "ep_dispatch_ll")
+                                 p["slot"], st), "ep_dispatch_ll")
         rec(2)
-        check(lib.ep_combine_ll(cp, cap, p["y"], p["slot"], p["wt"], p["out"], sh), "ep_combine_ll")
+        check(lib.ep_combine_ll(cp, cap, p["y"], p["slot"], p["wt"], p["out"], st), "ep_combine_ll")
         rec(3)
 
     stages = ("route", "dispatch_ll", "combine_ll")
     dur, wall = timed_steps(args, nsets, launch, stages)
+    graph_us = graph_step_us(args, nsets, lambda i, st: launch(i, lambda q: None, int(st)))
     kt = kernel_table(dur, bytes_)
     avg = {s: kt[s]["avg_us"] * 1e-6 for s in stages}
     dc_time = avg["dispatch_ll"] + avg["combine_ll"]
@@ -446,6 +448,7 @@ def run_ll(args, w):
                    "combine": "bf16_fp32_accumulate", "buffer_sets": nsets},
         "dispatch_combine_gbs": round(dc_bytes / dc_time / 1e9, 1),
         "step_us": round(sum(avg.values()) * 1e6, 2),
+        "graph_step_us": round(graph_us, 2),
         "roofline": {"kernel": "combine_ll", "bound": "hbm", "achieved": round(comb_gbs, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(comb_gbs / HBM_PEAK_GBS, 4),
                      "traffic": None},
