@@ -687,7 +687,7 @@ def run_dedup(args, w):
 def main():
     args = parse()
     if args.gpus != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
+        print("bench.py measures one GPU only: the library has no multi-GPU exchange "
               "(--gpus %d requested)" % args.gpus, file=sys.stderr)
         return 2
     if args.copy_probe:
