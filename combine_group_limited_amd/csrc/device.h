@@ -84,9 +84,13 @@ constexpr int kDppXor2 = 0x4E;        // quad_perm [2,3,0,1]
 constexpr int kDppHalfMirror = 0x141; // lane i <-> 7 - i within 8
 constexpr int kDppMirror = 0x140;     // lane i <-> 15 - i within 16
 
+// Every lane's source lane is valid for these permutations, so the `old`
+// operand and bound_ctrl never take effect; old = 0 with bound_ctrl lets the
+// compiler fold the move into the consuming v_max/v_min (one DPP
+// instruction per butterfly step instead of three).
 template <int CTRL>
 __device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
-    return (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, CTRL, 0xF, 0xF, false);
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, true);
 }
 
 // Partner value across aligned lane groups of size 2D (D = 1 .. 32, a
@@ -104,17 +108,19 @@ __device__ __forceinline__ uint32_t partner_u32(uint32_t v) {
 }
 
 // Largest 32-bit unsigned value across a fully active wavefront, as a
-// wave-uniform value: row-wise butterfly with DPP, then the four row maxima.
+// wave-uniform value: row-wise butterfly with DPP, then two row broadcasts
+// (row_bcast:15 folds rows 0 -> 1 and 2 -> 3, row_bcast:31 row 1 -> rows 2
+// and 3; rows outside the row mask keep v), so lane 63 holds the maximum.
+constexpr int kDppRowBcast15 = 0x142;
+constexpr int kDppRowBcast31 = 0x143;
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
     v = max(v, dpp_u32<kDppXor1>(v));
     v = max(v, dpp_u32<kDppXor2>(v));
     v = max(v, dpp_u32<kDppHalfMirror>(v));
     v = max(v, dpp_u32<kDppMirror>(v));
-    const uint32_t a = (uint32_t)__builtin_amdgcn_readlane((int)v, 0);
-    const uint32_t b = (uint32_t)__builtin_amdgcn_readlane((int)v, 16);
-    const uint32_t c = (uint32_t)__builtin_amdgcn_readlane((int)v, 32);
-    const uint32_t d = (uint32_t)__builtin_amdgcn_readlane((int)v, 48);
-    return max(max(a, b), max(c, d));
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, kDppRowBcast15, 0xA, 0xF, false));
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, kDppRowBcast31, 0xC, 0xF, false));
+    return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
 }
 
 // Largest 64-bit value across the wavefront (every lane gets it).
