@@ -33,7 +33,7 @@ __global__ __launch_bounds__(kMaxBlockThreads) void dispatch_ll_kernel(
     const uint16_t* __restrict__ x, const int32_t* __restrict__ idx, void* __restrict__ recv,
     float* __restrict__ recv_sc, int32_t* __restrict__ recv_count, int32_t* __restrict__ recv_src,
     int32_t* __restrict__ slot_out, int T, int H, int E, int k, int cap) {
-    __shared__ int s_cnt[kMaxExpertsLL];  // expert counts (last block) or per-pick counts
+    __shared__ int s_cnt[kMaxExpertsLL];  // per-expert counts: of all pairs (last block) or of earlier pairs
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
