@@ -19,5 +19,6 @@ from .api import (  # noqa: F401
     layout_workspace_bytes,
     rank_layout_workspace_bytes,
     route,
+    scores,
     validate,
 )

@@ -34,6 +34,7 @@ EXPORTS = (
     "ep_last_hip_error",
     "ep_validate_config",
     "ep_route",
+    "ep_scores",
     "ep_layout_workspace_bytes",
     "ep_get_layout",
     "ep_dispatch",
@@ -88,6 +89,8 @@ def lib() -> ctypes.CDLL:
         L.ep_validate_config.restype = I
         L.ep_route.argtypes = [C, P, P, P, P]
         L.ep_route.restype = I
+        L.ep_scores.argtypes = [C, P, P, P]
+        L.ep_scores.restype = I
         L.ep_layout_workspace_bytes.argtypes = [C]
         L.ep_layout_workspace_bytes.restype = ctypes.c_size_t
         L.ep_get_layout.argtypes = [C, P, P, P, P, P, P, P, ctypes.c_size_t, P]

@@ -100,6 +100,19 @@ def route(cfg: Config, logits: torch.Tensor, topk_idx=None, topk_w=None, stream=
     return topk_idx, topk_w
 
 
+def scores(cfg: Config, logits: torch.Tensor, out=None, stream=None) -> torch.Tensor:
+    """The gate's sigmoid scores, fp32 [T, E], bit-equal to those ep_route
+    ranks.  `out` may be `logits` itself (in place)."""
+    dev = logits.device
+    _want(logits, "logits", (cfg.T, cfg.E), torch.float32, None)
+    if out is None:
+        out = torch.empty((cfg.T, cfg.E), dtype=torch.float32, device=dev)
+    _want(out, "scores", (cfg.T, cfg.E), torch.float32, dev)
+    c = cfg.c()
+    _check(L.lib().ep_scores(ctypes.byref(c), _ptr(logits), _ptr(out), _stream(stream, dev)), "ep_scores")
+    return out
+
+
 def layout_workspace_bytes(cfg: Config) -> int:
     c = cfg.c()
     return int(L.lib().ep_layout_workspace_bytes(ctypes.byref(c)))

@@ -97,6 +97,14 @@ EP_API int ep_route(const ep_config_t* cfg, const float* logits, int32_t* topk_i
                                        static_cast<hipStream_t>(stream)));
 }
 
+EP_API int ep_scores(const ep_config_t* cfg, const float* logits, float* scores, void* stream) {
+    int rc = validate(cfg);
+    if (rc) return rc;
+    if (cfg->num_tokens > 0 && (!logits || !scores)) return EP_ERR_INVALID_ARG;
+    if (!aligned(logits, 4) || !aligned(scores, 4)) return EP_ERR_ALIGNMENT;
+    return hip_status(ep::launch_scores(shape_of(cfg), logits, scores, static_cast<hipStream_t>(stream)));
+}
+
 EP_API size_t ep_layout_workspace_bytes(const ep_config_t* cfg) {
     if (validate(cfg)) return 0;
     return ep::layout_workspace_bytes(shape_of(cfg));

@@ -295,6 +295,30 @@ hipError_t launch_fast_mc(const Shape& s, int mc, int gs_log2, const float* logi
     return launch_fast<EPL, 2>(s, gs_log2, logits, idx, w, st);
 }
 
+// Elementwise gate scores, V consecutive values per lane per step (V = 4
+// when both pointers are 16-byte aligned), grid-stride over the T*E values.
+// No __restrict__: scores may alias logits.
+template <int V>
+__global__ __launch_bounds__(256) void scores_kernel(const float* logits, float* scores, size_t n) {
+    const size_t stride = (size_t)gridDim.x * blockDim.x;
+    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i * V < n; i += stride) {
+        if (V == 4 && i * 4 + 4 <= n) {
+            float4 v = reinterpret_cast<const float4*>(logits)[i];
+            v.x = sigmoid(v.x);
+            v.y = sigmoid(v.y);
+            v.z = sigmoid(v.z);
+            v.w = sigmoid(v.w);
+            reinterpret_cast<float4*>(scores)[i] = v;
+        } else {
+#pragma unroll
+            for (int u = 0; u < V; ++u) {
+                const size_t j = i * V + u;
+                if (j < n) scores[j] = sigmoid(logits[j]);
+            }
+        }
+    }
+}
+
 }  // namespace
 
 hipError_t launch_route(const Shape& s, const float* logits, int32_t* topk_idx, float* topk_w,
@@ -319,6 +343,21 @@ hipError_t launch_route(const Shape& s, const float* logits, int32_t* topk_idx, 
     if (epl <= 4) return launch_gate<4>(s, logits, topk_idx, topk_w, stream);
     if (epl <= 8) return launch_gate<8>(s, logits, topk_idx, topk_w, stream);
     return launch_gate<16>(s, logits, topk_idx, topk_w, stream);
+}
+
+hipError_t launch_scores(const Shape& s, const float* logits, float* scores, hipStream_t stream) {
+    const size_t n = (size_t)s.T * (size_t)s.E;
+    if (n == 0) return hipSuccess;
+    const bool vec = ((reinterpret_cast<uintptr_t>(logits) | reinterpret_cast<uintptr_t>(scores)) & 15) == 0;
+    const int V = vec ? 4 : 1;
+    const size_t lanes = (n + V - 1) / V;
+    const size_t want = (lanes + 255) / 256;
+    const unsigned blocks = (unsigned)(want < (1u << 16) ? want : (1u << 16));
+    if (vec)
+        hipLaunchKernelGGL(scores_kernel<4>, dim3(blocks), dim3(256), 0, stream, logits, scores, n);
+    else
+        hipLaunchKernelGGL(scores_kernel<1>, dim3(blocks), dim3(256), 0, stream, logits, scores, n);
+    return hipGetLastError();
 }
 
 }  // namespace ep

@@ -17,6 +17,7 @@ struct Shape {
 
 hipError_t launch_route(const Shape& s, const float* logits, int32_t* topk_idx, float* topk_w,
                         hipStream_t stream);
+hipError_t launch_scores(const Shape& s, const float* logits, float* scores, hipStream_t stream);
 
 size_t layout_workspace_bytes(const Shape& s);
 hipError_t launch_layout(const Shape& s, const int32_t* topk_idx, int32_t* cnt, int32_t* ntok_rank,

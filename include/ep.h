@@ -54,7 +54,7 @@ extern "C" {
 
 #define EP_API __attribute__((visibility("default")))
 
-#define EP_ABI_VERSION 1
+#define EP_ABI_VERSION 2
 
 /* Return codes */
 #define EP_OK               0
@@ -120,6 +120,17 @@ EP_API int ep_validate_config(const ep_config_t* cfg);
  * Alignment: 4 bytes.  Kernel: one 64-lane wavefront per token. */
 EP_API int ep_route(const ep_config_t* cfg, const float* logits,
                     int32_t* topk_idx, float* topk_w, void* stream);
+
+/* The gate's scores alone ([NEWS] feature list; [DE]): the router
+ * probabilities that ep_route ranks, for callers that need them as well
+ * (an auxiliary load-balancing loss, logging).
+ *   logits    device, fp32 [T, E]
+ *   scores    device, fp32 [T, E]  out: s = 1 / (1 + exp(-logit)), computed
+ *             exactly as ep_route computes it (same exp, same roundings),
+ *             so the bits equal those ep_route ranks
+ * May alias logits (in place).  Alignment: 4 bytes.  Kernel: elementwise,
+ * four values per lane when both pointers are 16-byte aligned. */
+EP_API int ep_scores(const ep_config_t* cfg, const float* logits, float* scores, void* stream);
 
 /* Bytes of device workspace ep_get_layout needs for `cfg` (0 if invalid). */
 EP_API size_t ep_layout_workspace_bytes(const ep_config_t* cfg);

@@ -29,7 +29,7 @@ def test_every_declared_function_is_exported():
 
 def test_version_and_messages():
     lib = ep.lib()
-    assert lib.ep_abi_version() == 1
+    assert lib.ep_abi_version() == 2
     for code in (0, -1, -2, -3, -4, -5, 42):
         assert len(lib.ep_strerror(code)) > 0
     assert lib.ep_last_hip_error() == 0
@@ -97,6 +97,20 @@ def test_route_rejections():
     # nothing to do for zero tokens: succeeds without touching the GPU
     z = _cfg(T=0).c()
     assert lib.ep_route(ctypes.byref(z), None, None, None, None) == L.EP_OK
+
+
+def test_scores_rejections():
+    lib = ep.lib()
+    c = _cfg().c()
+    assert lib.ep_scores(ctypes.byref(c), None, FAKE, None) == L.EP_ERR_INVALID_ARG
+    assert lib.ep_scores(ctypes.byref(c), FAKE, None, None) == L.EP_ERR_INVALID_ARG
+    assert lib.ep_scores(ctypes.byref(c), FAKE + 2, FAKE, None) == L.EP_ERR_ALIGNMENT
+    assert lib.ep_scores(ctypes.byref(c), FAKE, FAKE + 1, None) == L.EP_ERR_ALIGNMENT
+    bad = _cfg(H=100).c()
+    assert lib.ep_scores(ctypes.byref(bad), FAKE, FAKE, None) == L.EP_ERR_INVALID_ARG
+    assert lib.ep_scores(None, FAKE, FAKE, None) == L.EP_ERR_INVALID_ARG
+    z = _cfg(T=0).c()
+    assert lib.ep_scores(ctypes.byref(z), None, None, None) == L.EP_OK
 
 
 def test_layout_rejections():
