@@ -129,25 +129,33 @@ def buffer_sets(requested: int, touched: int, allocated: int) -> int:
     return int(n)
 
 
-def copy_probe():
-    """A plain copy of known size: 5 x 1 GiB device-to-device copies.  Its
-    FETCH_SIZE / WRITE_SIZE readings give the factor between those counters
-    and bytes actually moved."""
+def _copy_gbs(n: int = 1 << 30, reps: int = 5):
+    """(microseconds, GB/s read + written) of a plain n-byte device-to-device
+    copy, averaged over `reps` copies after one untimed copy."""
     import torch
-    n = 1 << 30
     a = torch.ones(n, dtype=torch.uint8, device="cuda")
     b = torch.empty_like(a)
     s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     b.copy_(a)
     torch.cuda.synchronize()
     s.record()
-    for _ in range(5):
+    for _ in range(reps):
         b.copy_(a)
     e.record()
     torch.cuda.synchronize()
-    t = s.elapsed_time(e) / 5 * 1e-3
+    t = s.elapsed_time(e) / reps * 1e-3
+    del a, b
+    return t * 1e6, 2 * n / t / 1e9
+
+
+def copy_probe():
+    """A plain copy of known size: 5 x 1 GiB device-to-device copies.  Its
+    FETCH_SIZE / WRITE_SIZE readings give the factor between those counters
+    and bytes actually moved."""
+    n = 1 << 30
+    us, gbs = _copy_gbs(n)
     print(json.dumps({"kind": "copy_probe", "bytes_read": n, "bytes_written": n,
-                      "us": round(t * 1e6, 1), "gbs_read_plus_write": round(2 * n / t / 1e9, 1)}), flush=True)
+                      "us": round(us, 1), "gbs_read_plus_write": round(gbs, 1)}), flush=True)
     return 0
 
 
@@ -341,6 +349,9 @@ def run_normal(args, w):
         "step_tokens_per_s": round(w.T / (wall / args.steps), 1),
         "graph_step_us": round(graph_us, 2),
         "graph_step_tokens_per_s": round(w.T / (graph_us * 1e-6), 1),
+        "context": {"device_copy_gbs": round(_copy_gbs()[1], 1),
+                    "note": "plain 1 GiB device-to-device copy, bytes read + written per second: "
+                            "a practical ceiling beside the 8000 GB/s peak"},
         "roofline": {"kernel": "combine", "bound": "hbm", "achieved": round(comb_gbs, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(comb_gbs / HBM_PEAK_GBS, 4),
                      "traffic": _recorded_traffic("combine", w.name)},
