@@ -105,7 +105,7 @@ def parse():
                     help="normal: route + layout + dispatch + combine; ll: route + dispatch_ll + combine_ll; "
                          "overlap: dispatch + combine on a CU budget next to a bf16 GEMM on the other CUs; "
                          "dedup: per-rank deduplicated dispatch + in-rank partial combine + combine of partials")
-    ap.add_argument("--cus", default="32,64,128,192", help="CU budgets of the overlap path")
+    ap.add_argument("--cus", default="16,24,32,64,128", help="CU budgets of the overlap path")
     ap.add_argument("--gemm-n", type=int, default=14336, help="output width of the overlap path's GEMM")
     ap.add_argument("--recv-dtype", choices=("fp8", "bf16"), default="fp8", help="dispatch payload")
     ap.add_argument("--capacity", type=int, default=0, help="low-latency rows per expert (0: T)")

@@ -244,21 +244,29 @@ EP_API int ep_stream_create_cu_range(int first_cu, int num_cus, void** stream) {
     int dev = 0, ncu = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e == hipSuccess) e = hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
-    if (e != hipSuccess) return hip_status(e);
+    if (e != hipSuccess) {
+        (void)hipGetLastError();  // the error is returned here, not left pending for the next call
+        return hip_status(e);
+    }
     if ((long)first_cu + num_cus > ncu) return EP_ERR_INVALID_ARG;
     uint32_t mask[64] = {0};  // up to 2048 CUs
     if (ncu > 64 * 32) return EP_ERR_UNSUPPORTED;
     for (int cu = first_cu; cu < first_cu + num_cus; ++cu) mask[cu >> 5] |= 1u << (cu & 31);
     hipStream_t st = nullptr;
     e = hipExtStreamCreateWithCUMask(&st, (uint32_t)((ncu + 31) / 32), mask);
-    if (e != hipSuccess) return hip_status(e);
+    if (e != hipSuccess) {
+        (void)hipGetLastError();
+        return hip_status(e);
+    }
     *stream = st;
     return EP_OK;
 }
 
 EP_API int ep_stream_destroy(void* stream) {
     if (!stream) return EP_ERR_INVALID_ARG;
-    return hip_status(hipStreamDestroy(static_cast<hipStream_t>(stream)));
+    const hipError_t e = hipStreamDestroy(static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) (void)hipGetLastError();
+    return hip_status(e);
 }
 
 }  // extern "C"

@@ -37,7 +37,10 @@
  *    overlap.
  *  - Errors: negative return codes (below); validation happens before any
  *    HIP call, so an invalid call has no effect.  EP_ERR_HIP reports a
- *    failed kernel launch (ep_last_hip_error gives the hipError_t).
+ *    failed kernel launch (ep_last_hip_error gives the hipError_t); the
+ *    launch status is read with hipGetLastError, so an error that an
+ *    earlier HIP call on the same thread left pending is reported (and
+ *    cleared) by the next call here.
  *    Faults inside kernels surface as HIP errors at the caller's next
  *    synchronisation, as for any HIP kernel.
  *  - Calls are reentrant and keep no state between calls.
@@ -296,7 +299,10 @@ EP_API int ep_combine_ranks(const ep_config_t* cfg, const void* partial, const i
  * device; pass it as `stream` to the calls above to cap the CUs they use,
  * and give the remaining CUs to a compute stream made the same way.  The
  * stream has the default priority.  On MI355X the HIP runtime accepts only
- * contiguous CU ranges.
+ * contiguous CU ranges, and a range paces the kernels by steps of 32 CUs:
+ * dispatch + combine take the same time on 32 to 56 CUs and speed up again
+ * at 64 (measured), so budgets that are multiples of 32, or below 32, use
+ * their CUs best.  A refused stream leaves no pending HIP error behind.
  *   first_cu, num_cus  0 <= first_cu, num_cus >= 1,
  *                      first_cu + num_cus <= the device's CU count
  *   stream             host, out: the new hipStream_t
