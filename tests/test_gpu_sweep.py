@@ -92,3 +92,38 @@ def test_random_config(case):
         o3 = ep.combine_ll(cfg, cap, to_dev(yll, torch.bfloat16), ll["slot"], wt)
         torch.cuda.synchronize()
         assert bf16_ulp_diff(to_host(o3), oracle.combine(yll, oll["slot"], ow)).max() <= 1
+
+
+def _tied_logits(rng, T, E, mode):
+    # few distinct values, so that scores and group scores tie exactly and
+    # the index rules decide; "ulps" adds 0-2 ulp steps, so that nearly
+    # equal logits map to equal or adjacent scores
+    vals = np.float32([-3.0, -0.5, 0.0, 0.75, 2.0])
+    lg = rng.choice(vals[: int(rng.integers(1, 6))], size=(T, E)).astype(np.float32)
+    if mode == "ulps":
+        steps = rng.integers(0, 3, size=(T, E)).astype(np.int32)
+        lg = (lg.view(np.int32) + np.where(lg >= 0, steps, -steps)).view(np.float32)
+    return lg
+
+
+@pytest.mark.parametrize("case", range(16))
+def test_random_config_tied_logits(case):
+    rng = np.random.default_rng(5000 + case)
+    w = _draw(rng)
+    mode = "ulps" if case % 2 else "exact"
+    cfg = ep.Config.of(w)
+    print("tied sweep", case, mode, w, flush=True)
+    lg = _tied_logits(rng, w.T, w.E, mode)
+    idx, wt = ep.route(cfg, to_dev(lg))
+    lay = ep.get_layout(cfg, idx)
+    rl = ep.get_rank_layout(cfg, idx)
+    torch.cuda.synchronize()
+    oi, ow = oracle.route(lg, w.G, w.TG, w.k, w.topm)
+    assert np.array_equal(to_host(idx), oi)
+    assert np.array_equal(to_host(wt).view(np.uint32), ow.view(np.uint32))
+    ol = oracle.layout(oi, w.E, w.R)
+    for key in ("cnt", "off", "ntok_rank", "slot", "recv_token"):
+        assert np.array_equal(to_host(lay[key]), ol[key]), key
+    orl = oracle.rank_layout(oi, w.E, w.R)
+    for key in ("rank_count", "rank_offset", "rank_slot", "rank_token"):
+        assert np.array_equal(to_host(rl[key]), orl[key]), key
