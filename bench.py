@@ -199,8 +199,8 @@ def launch_step(lib, cp, p, code, ws, nws, sh, check):
 
 def graph_step_us(args, nsets, step_on):
     """Average time of one step replayed from a captured HIP graph.  One
-    graph holds one step per buffer set, in order, so a replay runs `nsets`
-    steps back to back and the graph's own launch cost is spread over them,
+    graph holds at least 8 steps, cycling through the buffer sets (a whole
+    number of cycles), so the graph's own launch cost is spread over them,
     as when a loop of steps is captured; events around all replays."""
     import torch
     side = torch.cuda.Stream()
@@ -209,13 +209,14 @@ def graph_step_us(args, nsets, step_on):
         step_on(0, side.cuda_stream)
     torch.cuda.current_stream().wait_stream(side)
     torch.cuda.synchronize()
+    per_graph = nsets * -(-8 // nsets)
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
-        for i in range(nsets):
-            step_on(i, torch.cuda.current_stream().cuda_stream)
+        for i in range(per_graph):
+            step_on(i % nsets, torch.cuda.current_stream().cuda_stream)
     g.replay()
     torch.cuda.synchronize()
-    reps = max(1, -(-max(args.steps, 1) // nsets))
+    reps = max(1, -(-max(args.steps, 1) // per_graph))
     hev = HipEvents()
     e = hev.create(2)
     sh = int(torch.cuda.current_stream().cuda_stream)
@@ -223,7 +224,7 @@ def graph_step_us(args, nsets, step_on):
     for _ in range(reps):
         g.replay()
     hev.record(e[1], sh)
-    t = hev.seconds(e[0], e[1]) / (reps * nsets)
+    t = hev.seconds(e[0], e[1]) / (reps * per_graph)
     hev.destroy(e)
     del g
     return t * 1e6
