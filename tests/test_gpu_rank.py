@@ -86,3 +86,17 @@ def test_rank_path_unrouted_and_repeated():
     idx[rng.random(idx.shape) < 0.03] = w.E + 2
     wt = rng.random((w.T, w.k)).astype(np.float32)
     run_and_check(w, idx, wt, W.gen_x(w), W.gen_y(w))
+
+
+def test_rank_layout_large_batch():
+    # 16384 tokens x top-8 = 131072 picks: the layout over the 32 rank
+    # buckets takes the three-launch path (more than 64 count blocks)
+    w = W.LARGE
+    say("rank layout large", w)
+    idx, _ = oracle.route(W.gen_logits(w), w.G, w.TG, w.k, w.topm)
+    cfg = ep.Config.of(w)
+    rl = ep.get_rank_layout(cfg, to_dev(idx))
+    torch.cuda.synchronize()
+    orl = oracle.rank_layout(idx, w.E, w.R)
+    for key in ("rank_count", "rank_offset", "rank_slot", "rank_token"):
+        assert np.array_equal(to_host(rl[key]), orl[key]), key
