@@ -44,7 +44,9 @@ inline int layout_blocks(long P, int W) { return (int)((P + 64 * W - 1) / (64 * 
 // separate scan.
 constexpr int kSelfScanMaxBlocks = 64;
 
-// pairs up to which one workgroup does the whole layout in one launch.
+// pairs up to which one workgroup does the whole layout in one launch
+// (from 513 pairs a 1024-thread workgroup, when its LDS fits, so that all
+// pairs are ranked in one chunk: 1024 pairs 6.8 -> 6.6 us).
 // Measured per call on MI355X, 256 experts, top-8: 256 pairs 8.6 -> 5.7 us,
 // 1024 pairs 8.0 -> 6.9 us; at 2048 pairs one workgroup is slower (9.0
 // against 8.2 us).
@@ -434,6 +436,13 @@ hipError_t launch_layout(const Shape& s, const int32_t* topk_idx, int32_t* cnt, 
     int32_t* hist = static_cast<int32_t*>(ws);
     int32_t* rk = hist + (size_t)s.E * C;
     const size_t small_lds = (size_t)(12 * W + 4) * s.E + (size_t)P * sizeof(int32_t);
+    const size_t wide_lds = (size_t)(12 * 16 + 4) * s.E + (size_t)P * sizeof(int32_t);
+    if (P > 512 && P <= kSmallMaxPairs && wide_lds <= kSmallMaxLds) {
+        // one 1024-thread workgroup ranks up to 1024 pairs in a single chunk
+        hipLaunchKernelGGL(layout_small_kernel<16>, dim3(1), dim3(16 * 64), wide_lds, stream, topk_idx, cnt, ntok_rank,
+                           off, slot, recv_token, P, s.k, s.E, s.R, s.E / s.R);
+        return hipGetLastError();
+    }
     if (P <= kSmallMaxPairs && small_lds <= kSmallMaxLds) {
         const size_t lds = small_lds;
         if (W == 8)
