@@ -49,6 +49,8 @@ def lib() -> ctypes.CDLL:
         F = ctypes.c_float
         L.orc_expf.argtypes = [F]; L.orc_expf.restype = F
         L.orc_sigmoid.argtypes = [F]; L.orc_sigmoid.restype = F
+        L.orc_expf_hi.argtypes = []; L.orc_expf_hi.restype = F
+        L.orc_expf_lo.argtypes = []; L.orc_expf_lo.restype = F
         L.orc_e4m3_from_f32.argtypes = [F]; L.orc_e4m3_from_f32.restype = ctypes.c_uint8
         L.orc_e4m3_to_f32.argtypes = [ctypes.c_uint8]; L.orc_e4m3_to_f32.restype = F
         L.orc_bf16_from_f32.argtypes = [F]; L.orc_bf16_from_f32.restype = ctypes.c_uint16

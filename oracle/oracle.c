@@ -11,6 +11,7 @@
  */
 #include "oracle.h"
 
+#include <float.h>
 #include <math.h>
 #include <stdlib.h>
 #include <string.h>
@@ -26,12 +27,18 @@ static float u2f(uint32_t u) { float f; memcpy(&f, &u, 4); return f; }
  *           n * C1 is exact for |n| < 2^12
  *   C2    = fp32(ln 2 - C1)
  *   P[i]  = fp32(1 / i!)
- * Range: x > 88 -> +inf, x < -86 -> 0, so n = rint(x * L2E) lies in
- * [-124, 127] and p * 2^n is a normal number, which makes the final scaling
- * exact.  NaN propagates.
+ *   HI    = the smallest fp32 x with e^x > FLT_MAX (e^x then rounds to
+ *           +inf), i.e. the first fp32 value above ln(FLT_MAX)
+ *   LO    = the smallest fp32 x with e^x >= 2^-126 (the smallest normal),
+ *           i.e. the first fp32 value at or above ln(2^-126)
+ * Range: x >= HI -> +inf; x < LO -> 0 (no subnormal results).  In between,
+ * n = rint(x * L2E) lies in [-126, 128]; p * 2^n is formed as
+ * (p * 2^n1) * 2^n2 with n1 = floor(n / 2), n2 = n - n1, both factors
+ * normal, so n = 128 (x just below HI) and n = -126 need no special case and
+ * every step is one correctly rounded operation.  NaN propagates.
  * ------------------------------------------------------------------------- */
 static int   g_consts_ready = 0;
-static float g_l2e, g_c1, g_c2, g_p[8];
+static float g_l2e, g_c1, g_c2, g_p[8], g_hi, g_lo;
 
 static void exp_consts(void) {
     if (g_consts_ready) return;
@@ -44,22 +51,34 @@ static void exp_consts(void) {
         if (i > 0) fact *= (double)i;
         g_p[i] = (float)(1.0 / fact);
     }
+    double ln_max = log((double)FLT_MAX);
+    g_hi = (float)ln_max;
+    if ((double)g_hi <= ln_max) g_hi = nextafterf(g_hi, INFINITY);
+    double ln_min = log(ldexp(1.0, -126));
+    g_lo = (float)ln_min;
+    if ((double)g_lo < ln_min) g_lo = nextafterf(g_lo, 0.0f);
     g_consts_ready = 1;
 }
+
+static float pow2i(int n) { return u2f((uint32_t)(n + 127) << 23); }  /* normal range only */
 
 float orc_expf(float x) {
     exp_consts();
     if (x != x) return x;
-    if (x > 88.0f) return INFINITY;
-    if (x < -86.0f) return 0.0f;
+    if (x >= g_hi) return INFINITY;
+    if (x < g_lo) return 0.0f;
     float n = rintf(x * g_l2e);
     float r = fmaf(-n, g_c1, x);
     r = fmaf(-n, g_c2, r);
     float p = g_p[7];
     for (int i = 6; i >= 0; --i) p = fmaf(p, r, g_p[i]);
-    int ni = (int)n;
-    return p * u2f((uint32_t)(ni + 127) << 23);
+    int n1 = (int)floorf(n * 0.5f);
+    int n2 = (int)n - n1;
+    return (p * pow2i(n1)) * pow2i(n2);
 }
+
+float orc_expf_hi(void) { exp_consts(); return g_hi; }
+float orc_expf_lo(void) { exp_consts(); return g_lo; }
 
 float orc_sigmoid(float x) {
     return 1.0f / (1.0f + orc_expf(-x));

@@ -38,8 +38,14 @@ extern "C" {
  * Taylor polynomial evaluated with fused multiply-add (W. J. Cody, W. Waite,
  * "Software Manual for the Elementary Functions", 1980).  Every step is one
  * correctly rounded IEEE-754 operation, so any implementation that follows
- * the same steps returns the same bits. */
+ * the same steps returns the same bits.  +inf from the first fp32 value
+ * whose exponential exceeds FLT_MAX (88.72283935546875); 0 below the first
+ * fp32 value whose exponential is a normal number (-87.33654022216797), so
+ * there are no subnormal results. */
 float orc_expf(float x);
+/* The two cut-offs above, as derived by the oracle from log(). */
+float orc_expf_hi(void);
+float orc_expf_lo(void);
 /* 1 / (1 + orc_expf(-x)), fp32, correctly rounded add and divide. */
 float orc_sigmoid(float x);
 /* fp32 -> OCP OFP8 E4M3 (bias 7, max 448, no infinities) with round to

@@ -26,43 +26,98 @@ def _sweep(lo: float, hi: float, n: int) -> np.ndarray:
     return x[(x >= lo) & (x <= hi)]
 
 
+# fp32's own range of the exponential, found from the mathematics in double
+# precision (not from the oracle): the first fp32 x whose e^x exceeds the
+# largest finite float, and the first whose e^x is at least the smallest
+# normal float 2^-126.
+def _first_f32_above(v: float, strict: bool) -> np.float32:
+    f = np.float32(v)
+    if float(f) < v or (strict and float(f) == v):
+        f = np.nextafter(f, np.float32(np.inf))
+    return f
+
+
+X_OVF = _first_f32_above(np.log(np.float64(np.finfo(np.float32).max)), strict=True)
+X_NORM = _first_f32_above(np.log(np.float64(2.0) ** -126), strict=False)
+
+
+def _edge(x0: np.float32, n: int) -> np.ndarray:
+    """The n fp32 values below x0 and x0 with the n - 1 above it."""
+    u = int(bits_from_f32([abs(x0)])[0])
+    v = f32_from_bits(np.arange(u - n, u + n, dtype=np.uint32))
+    return v if x0 > 0 else -v
+
+
+def test_expf_range_ends_are_fp32s():
+    # the whole polynomial path: n = rint(x log2 e) reaches 128 just below
+    # the overflow end and -126 at the normal end
+    assert float(X_OVF) == 88.72283935546875
+    assert float(X_NORM) == -87.33654022216797
+    with np.errstate(over="ignore"):
+        assert np.float32(np.exp(np.float64(X_OVF))) == np.inf
+        assert np.isfinite(np.float32(np.exp(np.float64(np.nextafter(X_OVF, np.float32(0))))))
+    assert np.exp(np.float64(X_NORM)) >= 2.0 ** -126
+    assert np.exp(np.float64(np.nextafter(X_NORM, np.float32(-np.inf)))) < 2.0 ** -126
+
+
 def test_expf_within_2ulp_of_double_exp():
-    x = _sweep(-86.0, 88.0, 4_000_000)
+    top = np.nextafter(X_OVF, np.float32(0))
+    x = np.concatenate([_sweep(float(X_NORM), float(top), 4_000_000),
+                        _edge(X_OVF, 1 << 16), _edge(X_NORM, 1 << 16)])
+    x = x[(x >= X_NORM) & (x < X_OVF)]
     got = oracle.expf(x).astype(np.float64)
     ref = np.exp(x.astype(np.float64))
     err = np.abs(got - ref) / f32_ulp(ref)
     assert err.max() <= 2.0, (x[np.argmax(err)], err.max())
+    assert np.all(got >= 2.0 ** -126) and np.all(np.isfinite(got))   # normal results only
     # dense around 0, where the reduction does nothing
     x = np.linspace(-1, 1, 200_001, dtype=np.float32)
     err = np.abs(oracle.expf(x) - np.exp(x.astype(np.float64))) / f32_ulp(np.exp(x.astype(np.float64)))
     assert err.max() <= 2.0
 
 
+def test_expf_zero_and_inf_exactly_outside_the_normal_range():
+    # +inf exactly where e^x rounds to +inf in fp32; 0 exactly where e^x is
+    # below the smallest normal (the stated reading: no subnormal results)
+    x = np.concatenate([_sweep(-110.0, 110.0, 400_000), _edge(X_OVF, 4096), _edge(X_NORM, 4096),
+                        np.float32([np.inf, -np.inf, 1e30, -1e30])])
+    got = oracle.expf(x)
+    with np.errstate(over="ignore"):
+        ref = np.exp(x.astype(np.float64))
+        assert np.array_equal(np.isinf(got), np.float32(ref) == np.inf)
+    assert np.array_equal(got == 0.0, ref < 2.0 ** -126)
+
+
 def test_expf_monotone_and_special_values():
-    x = np.sort(_sweep(-86.0, 88.0, 1_000_000))
+    x = np.sort(np.concatenate([_sweep(-100.0, 100.0, 1_000_000), _edge(X_OVF, 2048), _edge(X_NORM, 2048)]))
     y = oracle.expf(x)
-    assert np.all(np.diff(y.astype(np.float64)) >= 0)
+    assert np.all(y[1:] >= y[:-1])   # (+inf >= +inf holds; a difference would be NaN)
     assert oracle.expf(np.float32([0.0]))[0] == 1.0
-    assert np.isfinite(oracle.expf(np.float32([88.0]))[0])
-    assert oracle.expf(np.float32([np.nextafter(np.float32(88), np.float32(89))]))[0] == np.inf
-    assert oracle.expf(np.float32([-86.0]))[0] > 0
-    assert oracle.expf(np.float32([np.nextafter(np.float32(-86), np.float32(-87))]))[0] == 0.0
     assert np.isnan(oracle.expf(np.float32([np.nan]))[0])
+    assert oracle.expf(np.float32([-np.inf]))[0] == 0.0 and oracle.expf(np.float32([np.inf]))[0] == np.inf
+
+
+def test_oracle_cutoffs_equal_the_mathematical_ones():
+    assert oracle.lib().orc_expf_hi() == X_OVF
+    assert oracle.lib().orc_expf_lo() == X_NORM
 
 
 def test_sigmoid_range_monotone_and_accuracy():
-    x = np.sort(_sweep(-100.0, 100.0, 1_000_000))
+    x = np.sort(np.concatenate([_sweep(-100.0, 100.0, 1_000_000), _edge(-X_OVF, 4096), _edge(X_NORM, 4096)]))
     s = oracle.sigmoid(x)
     assert np.all(s >= 0) and np.all(s <= 1)
     assert np.all(np.diff(s.astype(np.float64)) >= 0)
     assert oracle.sigmoid(np.float32([0.0]))[0] == 0.5
-    ref = 1.0 / (1.0 + np.exp(-x.astype(np.float64)))
-    mid = (x > -80) & (x < 80)
-    err = np.abs(s[mid] - ref[mid]) / f32_ulp(ref[mid])
-    assert err.max() <= 3.0
-    # the definition's range cut-offs
-    assert oracle.sigmoid(np.float32([-89.0]))[0] == 0.0
-    assert oracle.sigmoid(np.float32([87.0]))[0] == 1.0
+    # within 3 ulp of the double sigmoid wherever fp32's e^-x is finite,
+    # including the subnormal results of 1 / (1 + e^-x) below x = -87.34
+    # (an ulp there is 2^-149)
+    fin = x > -X_OVF
+    ref = 1.0 / (1.0 + np.exp(-x[fin].astype(np.float64)))
+    err = np.abs(s[fin] - ref) / f32_ulp(ref)
+    assert err.max() <= 3.0, (x[fin][np.argmax(err)], err.max())
+    assert np.any(s[fin] < 2.0 ** -126)   # the subnormal results are reached
+    # below -88.7228 fp32's e^-x is +inf, and 1 / (1 + inf) is 0
+    assert np.all(s[~fin] == 0.0)
 
 
 # --------------------------------------------------------------- E4M3 ----
