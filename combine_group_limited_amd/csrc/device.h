@@ -43,16 +43,26 @@ __device__ __forceinline__ uint32_t pack_e4m3x4(float a, float b, float c, float
     return (uint32_t)w;
 }
 
+// 2^n for n in the normal exponent range [-126, 127], from its bit pattern.
+__device__ __forceinline__ float pow2_normal(int n) { return __uint_as_float((uint32_t)(n + 127) << 23); }
+
 // exp(x), fp32, by Cody & Waite additive range reduction and a degree-7
 // Taylor polynomial in Horner form with fused multiply-add.  Constants:
 // L2E = fp32(log2 e); C1 = fp32(ln 2) with its low 12 significand bits
-// cleared (n * C1 exact); C2 = fp32(ln 2 - C1); P_i = fp32(1 / i!).  For
-// x in [-86, 88] the scale 2^n is a normal number and the final multiply is
-// exact; beyond that the result is 0 or +inf.
+// cleared (n * C1 exact); C2 = fp32(ln 2 - C1); P_i = fp32(1 / i!).
+// Range: +inf from 88.72283935546875 (the first fp32 value whose exponential
+// exceeds FLT_MAX); 0 below -87.33654022216797 (the first fp32 value whose
+// exponential is a normal number), so results are never subnormal.  In
+// between n = rint(x * L2E) lies in [-126, 128], and 2^n is applied as two
+// normal factors 2^n1 * 2^n2 (n1 = floor(n / 2)), so n = 128 needs no
+// special case; every step is one correctly rounded operation.
 __device__ __forceinline__ float cw_expf(float x) {
-    // branch-free: the polynomial path runs on x clamped to [-86, 88] (where
-    // it equals x) and the out-of-range results are selected afterwards
-    const float xc = __builtin_fminf(__builtin_fmaxf(x, -86.0f), 88.0f);
+    constexpr float kLastFinite = 0x1.62e42ep+6f;  // largest fp32 with a finite exponential
+    constexpr float kFirstNormal = -0x1.5d589ep+6f;  // smallest fp32 with a normal exponential
+    // branch-free: the polynomial path runs on x clamped to the finite,
+    // normal range (where it equals x) and the out-of-range results are
+    // selected afterwards
+    const float xc = __builtin_fminf(__builtin_fmaxf(x, kFirstNormal), kLastFinite);
     const float L2E = 0x1.715476p+0f;
     const float C1 = 0x1.62ep-1f;
     const float C2 = 0x1.0bfbe8p-15f;
@@ -67,9 +77,11 @@ __device__ __forceinline__ float cw_expf(float x) {
     p = __builtin_fmaf(p, r, 0.5f);             // 1/2!
     p = __builtin_fmaf(p, r, 1.0f);             // 1/1!
     p = __builtin_fmaf(p, r, 1.0f);             // 1/0!
-    float y = p * __uint_as_float((uint32_t)((int)n + 127) << 23);
-    y = x > 88.0f ? __builtin_huge_valf() : y;
-    y = x < -86.0f ? 0.0f : y;
+    const int n1 = (int)__builtin_floorf(n * 0.5f);
+    const int n2 = (int)n - n1;
+    float y = (p * pow2_normal(n1)) * pow2_normal(n2);
+    y = x > kLastFinite ? __builtin_huge_valf() : y;
+    y = x < kFirstNormal ? 0.0f : y;
     return __builtin_isnan(x) ? x : y;
 }
 

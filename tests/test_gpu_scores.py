@@ -1,6 +1,6 @@
 """ep_scores against the oracle's sigmoid, bit for bit: a dense sweep of
-fp32 logits over [-100, 100] (every binade, both saturation regions, the
-cut-offs of the exponential) and special values, on the four-wide and the
+fp32 logits over [-100, 100] (every binade, both saturation regions, every
+pattern near the cut-offs of the exponential) and special values, on the four-wide and the
 scalar kernel path, in place and out of place; and the scores ep_route
 ranks: its weights are the chosen scores over their ordered sum."""
 import numpy as np
@@ -22,10 +22,15 @@ def sweep_values():
     # every 61st fp32 bit pattern from +0 to 100.0, both signs, and the
     # exponential's cut-offs with their neighbours
     pos = np.arange(0, 0x42C80001, 61, dtype=np.uint32).view(np.float32)
-    edges = np.float32([88.0, -88.0, 86.0, -86.0, 88.72283935546875, -87.33654475, 0.0, -0.0,
-                        np.inf, -np.inf, 1e-45, -1e-45, 17.0, -17.0, 104.0, -104.0])
+    edges = np.float32([88.72283935546875, -88.72283935546875, -87.33654022216797, 87.33654022216797,
+                        88.0, -88.0, 0.0, -0.0, np.inf, -np.inf, 1e-45, -1e-45, 17.0, -17.0, 104.0, -104.0])
     near = np.concatenate([np.nextafter(edges[:6], np.float32(np.inf)), np.nextafter(edges[:6], np.float32(-np.inf))])
-    return np.concatenate([pos, -pos, edges, near.astype(np.float32)])
+    # every fp32 pattern within 4096 of the exponential's range ends (logit
+    # -x reaches them), where the two-factor scaling and the subnormal
+    # sigmoid results are
+    u = np.concatenate([np.arange(b - 4096, b + 4096, dtype=np.uint32) for b in (0x42B17218, 0x42AEAC4F)])
+    dense = u.view(np.float32)
+    return np.concatenate([pos, -pos, edges, near.astype(np.float32), dense, -dense])
 
 
 def check(got, ref, name):
