@@ -31,7 +31,6 @@ __global__ __launch_bounds__(64, 8) void combine_kernel(const uint16_t* __restri
                                                       uint16_t* __restrict__ out, int H, int k, int nrows,
                                                       int segs, int items) {
     const int lane = threadIdx.x;
-    const int nchunks = H >> 3;
     const uint32_t row_bytes = (uint32_t)H * 2u;
     for (int item = blockIdx.x; item < items; item += gridDim.x) {
         const int t = item / segs;
@@ -44,50 +43,51 @@ __global__ __launch_bounds__(64, 8) void combine_kernel(const uint16_t* __restri
             if (!UNIT) my_w = w[(size_t)t * k + lane];
         }
 
-        if (chunk < nchunks) {
-            float acc[8];
+        // every lane takes part, also past the row end (its loads read zeros
+        // and its store is dropped by the row's buffer resource), so the
+        // v_readlane broadcasts below never run under a partial exec mask
+        float acc[8];
 #pragma unroll
-            for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
-            for (int j0 = 0; j0 < k; j0 += B) {
-                i32x4 v[B];
+        for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
+        for (int j0 = 0; j0 < k; j0 += B) {
+            i32x4 v[B];
 #pragma unroll
-                for (int j = 0; j < B; ++j) {
-                    v[j] = i32x4{0, 0, 0, 0};
-                    if (j0 + j < k) {
-                        const int r = __builtin_amdgcn_readlane(my_slot, j0 + j);
-                        if ((unsigned)r < (unsigned)nrows) {
-                            const auto yr = buffer_rsrc(y + (size_t)r * H, row_bytes);
-                            v[j] = __builtin_amdgcn_raw_buffer_load_b128(yr, chunk * 16, 0, kStream);
-                        }
-                    }
-                }
-#pragma unroll
-                for (int j = 0; j < B; ++j) {
-                    if (j0 + j < k) {
-                        const int r = __builtin_amdgcn_readlane(my_slot, j0 + j);
-                        if ((unsigned)r < (unsigned)nrows) {
-                            const float wj =
-                                __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(my_w), j0 + j));
-                            acc[0] = __builtin_fmaf(wj, bf16_lo(v[j].x), acc[0]);
-                            acc[1] = __builtin_fmaf(wj, bf16_hi(v[j].x), acc[1]);
-                            acc[2] = __builtin_fmaf(wj, bf16_lo(v[j].y), acc[2]);
-                            acc[3] = __builtin_fmaf(wj, bf16_hi(v[j].y), acc[3]);
-                            acc[4] = __builtin_fmaf(wj, bf16_lo(v[j].z), acc[4]);
-                            acc[5] = __builtin_fmaf(wj, bf16_hi(v[j].z), acc[5]);
-                            acc[6] = __builtin_fmaf(wj, bf16_lo(v[j].w), acc[6]);
-                            acc[7] = __builtin_fmaf(wj, bf16_hi(v[j].w), acc[7]);
-                        }
+            for (int j = 0; j < B; ++j) {
+                v[j] = i32x4{0, 0, 0, 0};
+                if (j0 + j < k) {
+                    const int r = __builtin_amdgcn_readlane(my_slot, j0 + j);
+                    if ((unsigned)r < (unsigned)nrows) {
+                        const auto yr = buffer_rsrc(y + (size_t)r * H, row_bytes);
+                        v[j] = __builtin_amdgcn_raw_buffer_load_b128(yr, chunk * 16, 0, kStream);
                     }
                 }
             }
-            i32x4 o;
-            o.x = (int)pack_bf16x2(acc[0], acc[1]);
-            o.y = (int)pack_bf16x2(acc[2], acc[3]);
-            o.z = (int)pack_bf16x2(acc[4], acc[5]);
-            o.w = (int)pack_bf16x2(acc[6], acc[7]);
-            const auto orr = buffer_rsrc(out + (size_t)t * H, row_bytes);
-            __builtin_amdgcn_raw_buffer_store_b128(o, orr, chunk * 16, 0, kStream);
+#pragma unroll
+            for (int j = 0; j < B; ++j) {
+                if (j0 + j < k) {
+                    const int r = __builtin_amdgcn_readlane(my_slot, j0 + j);
+                    if ((unsigned)r < (unsigned)nrows) {
+                        const float wj =
+                            __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(my_w), j0 + j));
+                        acc[0] = __builtin_fmaf(wj, bf16_lo(v[j].x), acc[0]);
+                        acc[1] = __builtin_fmaf(wj, bf16_hi(v[j].x), acc[1]);
+                        acc[2] = __builtin_fmaf(wj, bf16_lo(v[j].y), acc[2]);
+                        acc[3] = __builtin_fmaf(wj, bf16_hi(v[j].y), acc[3]);
+                        acc[4] = __builtin_fmaf(wj, bf16_lo(v[j].z), acc[4]);
+                        acc[5] = __builtin_fmaf(wj, bf16_hi(v[j].z), acc[5]);
+                        acc[6] = __builtin_fmaf(wj, bf16_lo(v[j].w), acc[6]);
+                        acc[7] = __builtin_fmaf(wj, bf16_hi(v[j].w), acc[7]);
+                    }
+                }
+            }
         }
+        i32x4 o;
+        o.x = (int)pack_bf16x2(acc[0], acc[1]);
+        o.y = (int)pack_bf16x2(acc[2], acc[3]);
+        o.z = (int)pack_bf16x2(acc[4], acc[5]);
+        o.w = (int)pack_bf16x2(acc[6], acc[7]);
+        const auto orr = buffer_rsrc(out + (size_t)t * H, row_bytes);
+        __builtin_amdgcn_raw_buffer_store_b128(o, orr, chunk * 16, 0, kStream);
     }
 }
 
@@ -113,7 +113,6 @@ __global__ __launch_bounds__(64, (KB <= 8 ? 8 : (KB <= 16 ? 4 : 2))) void combin
     const float* __restrict__ w, const int32_t* __restrict__ rank_slot, uint16_t* __restrict__ partial, int H, int k,
     int E, int EPR, int nrows, int segs, int items) {
     const int lane = threadIdx.x;
-    const int nchunks = H >> 3;
     const uint32_t row_bytes = (uint32_t)H * 2u;
     for (int item = blockIdx.x; item < items; item += gridDim.x) {
         const int t = item / segs;
@@ -136,52 +135,51 @@ __global__ __launch_bounds__(64, (KB <= 8 ? 8 : (KB <= 16 ? 4 : 2))) void combin
             if (rj >= 0 && rj == my_rank && (unsigned)sj < (unsigned)nrows) my_mask |= 1u << j;
         }
 
-        if (chunk < nchunks) {
-            i32x4 v[KB];
+        // every lane takes part (see combine_kernel)
+        i32x4 v[KB];
+#pragma unroll
+        for (int j = 0; j < KB; ++j) {
+            v[j] = i32x4{0, 0, 0, 0};
+            if (j < k) {
+                const int r = __builtin_amdgcn_readlane(my_slot, j);
+                if ((unsigned)r < (unsigned)nrows) {
+                    const auto yr = buffer_rsrc(y + (size_t)r * H, row_bytes);
+                    v[j] = __builtin_amdgcn_raw_buffer_load_b128(yr, chunk * 16, 0, kStream);
+                }
+            }
+        }
+        for (int jr = 0; jr < k; ++jr) {
+            const int prow = __builtin_amdgcn_readlane(my_rs, jr);
+            if ((unsigned)prow >= (unsigned)nrows) continue;  // not a first pick on its rank
+            const uint32_t m = (uint32_t)__builtin_amdgcn_readlane((int)my_mask, jr);
+            // keep the rows packed across the jr loop: unpacking all KB rows
+            // to fp32 once (hoisted out of the loop) would need 8*KB registers
+#pragma unroll
+            for (int j = 0; j < KB; ++j) asm volatile("" : "+v"(v[j]));
+            float acc[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
 #pragma unroll
             for (int j = 0; j < KB; ++j) {
-                v[j] = i32x4{0, 0, 0, 0};
-                if (j < k) {
-                    const int r = __builtin_amdgcn_readlane(my_slot, j);
-                    if ((unsigned)r < (unsigned)nrows) {
-                        const auto yr = buffer_rsrc(y + (size_t)r * H, row_bytes);
-                        v[j] = __builtin_amdgcn_raw_buffer_load_b128(yr, chunk * 16, 0, kStream);
-                    }
+                if ((m >> j) & 1u) {
+                    const float wj = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(my_w), j));
+                    acc[0] = __builtin_fmaf(wj, bf16_lo(v[j].x), acc[0]);
+                    acc[1] = __builtin_fmaf(wj, bf16_hi(v[j].x), acc[1]);
+                    acc[2] = __builtin_fmaf(wj, bf16_lo(v[j].y), acc[2]);
+                    acc[3] = __builtin_fmaf(wj, bf16_hi(v[j].y), acc[3]);
+                    acc[4] = __builtin_fmaf(wj, bf16_lo(v[j].z), acc[4]);
+                    acc[5] = __builtin_fmaf(wj, bf16_hi(v[j].z), acc[5]);
+                    acc[6] = __builtin_fmaf(wj, bf16_lo(v[j].w), acc[6]);
+                    acc[7] = __builtin_fmaf(wj, bf16_hi(v[j].w), acc[7]);
                 }
             }
-            for (int jr = 0; jr < k; ++jr) {
-                const int prow = __builtin_amdgcn_readlane(my_rs, jr);
-                if ((unsigned)prow >= (unsigned)nrows) continue;  // not a first pick on its rank
-                const uint32_t m = (uint32_t)__builtin_amdgcn_readlane((int)my_mask, jr);
-                // keep the rows packed across the jr loop: unpacking all KB rows
-                // to fp32 once (hoisted out of the loop) would need 8*KB registers
-#pragma unroll
-                for (int j = 0; j < KB; ++j) asm volatile("" : "+v"(v[j]));
-                float acc[8];
-#pragma unroll
-                for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
-#pragma unroll
-                for (int j = 0; j < KB; ++j) {
-                    if ((m >> j) & 1u) {
-                        const float wj = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(my_w), j));
-                        acc[0] = __builtin_fmaf(wj, bf16_lo(v[j].x), acc[0]);
-                        acc[1] = __builtin_fmaf(wj, bf16_hi(v[j].x), acc[1]);
-                        acc[2] = __builtin_fmaf(wj, bf16_lo(v[j].y), acc[2]);
-                        acc[3] = __builtin_fmaf(wj, bf16_hi(v[j].y), acc[3]);
-                        acc[4] = __builtin_fmaf(wj, bf16_lo(v[j].z), acc[4]);
-                        acc[5] = __builtin_fmaf(wj, bf16_hi(v[j].z), acc[5]);
-                        acc[6] = __builtin_fmaf(wj, bf16_lo(v[j].w), acc[6]);
-                        acc[7] = __builtin_fmaf(wj, bf16_hi(v[j].w), acc[7]);
-                    }
-                }
-                i32x4 o;
-                o.x = (int)pack_bf16x2(acc[0], acc[1]);
-                o.y = (int)pack_bf16x2(acc[2], acc[3]);
-                o.z = (int)pack_bf16x2(acc[4], acc[5]);
-                o.w = (int)pack_bf16x2(acc[6], acc[7]);
-                const auto pr = buffer_rsrc(partial + (size_t)prow * H, row_bytes);
-                __builtin_amdgcn_raw_buffer_store_b128(o, pr, chunk * 16, 0, kStream);
-            }
+            i32x4 o;
+            o.x = (int)pack_bf16x2(acc[0], acc[1]);
+            o.y = (int)pack_bf16x2(acc[2], acc[3]);
+            o.z = (int)pack_bf16x2(acc[4], acc[5]);
+            o.w = (int)pack_bf16x2(acc[6], acc[7]);
+            const auto pr = buffer_rsrc(partial + (size_t)prow * H, row_bytes);
+            __builtin_amdgcn_raw_buffer_store_b128(o, pr, chunk * 16, 0, kStream);
         }
     }
 }

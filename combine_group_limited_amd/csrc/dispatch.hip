@@ -29,7 +29,6 @@ __global__ __launch_bounds__(64, 8) void dispatch_fp8_kernel(const uint16_t* __r
                                                              float* __restrict__ recv_sc, int H, int k,
                                                              int nrows, int segs, int items, bool xcd_order) {
     const int lane = threadIdx.x;
-    const int nchunks = H >> 4;
     for (int v = blockIdx.x; v < items; v += gridDim.x) {
         const int item = xcd_order ? xcd_item(v, items) : v;
         const int t = item / segs;
@@ -39,8 +38,9 @@ __global__ __launch_bounds__(64, 8) void dispatch_fp8_kernel(const uint16_t* __r
         int my_slot = -1;
         if (lane < k) my_slot = slot[(size_t)t * k + lane];
 
-        // whole 8-lane groups fall outside the row together (H % 128 == 0)
-        if (chunk < nchunks) fp8_piece(x + (size_t)t * H, chunk, H, k, my_slot, nrows, recv, recv_sc);
+        // every lane takes part (pieces past the row end read zeros and
+        // store nothing), so the row-index broadcasts run on a full wave
+        fp8_piece(x + (size_t)t * H, chunk, H, k, my_slot, nrows, recv, recv_sc);
     }
 }
 
@@ -49,7 +49,6 @@ __global__ __launch_bounds__(64, 8) void dispatch_bf16_kernel(const uint16_t* __
                                                               uint16_t* __restrict__ recv, int H, int k,
                                                               int nrows, int segs, int items, bool xcd_order) {
     const int lane = threadIdx.x;
-    const int nchunks = H >> 3;
     for (int v = blockIdx.x; v < items; v += gridDim.x) {
         const int item = xcd_order ? xcd_item(v, items) : v;
         const int t = item / segs;
@@ -58,7 +57,7 @@ __global__ __launch_bounds__(64, 8) void dispatch_bf16_kernel(const uint16_t* __
         int my_slot = -1;
         if (lane < k) my_slot = slot[(size_t)t * k + lane];
 
-        if (chunk < nchunks) bf16_piece(x + (size_t)t * H, chunk, H, k, my_slot, nrows, recv);
+        bf16_piece(x + (size_t)t * H, chunk, H, k, my_slot, nrows, recv);
     }
 }
 

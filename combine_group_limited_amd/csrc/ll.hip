@@ -37,7 +37,6 @@ __global__ __launch_bounds__(kMaxBlockThreads) void dispatch_ll_kernel(
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
-    const int nw = blockDim.x >> 6;
 
     if (blockIdx.x == (unsigned)T) {  // per-expert counts of routed pairs
         const int P = T * k;
@@ -109,14 +108,17 @@ __global__ __launch_bounds__(kMaxBlockThreads) void dispatch_ll_kernel(
 
     const int nrows = E * cap;
     const int npieces = FP8 ? (H >> 4) : (H >> 3);
-    // 8-lane scale blocks stay together: H/16 and blockDim are multiples of 8
+    // a pass runs when any of its pieces lies in the row (a condition uniform
+    // over the workgroup); in it every lane stores (pieces past the row end
+    // were read as zeros and are dropped by the row's buffer resource; the
+    // scale store is guarded per lane), so the row-index broadcasts never
+    // run under a partial exec mask
 #pragma unroll
     for (int u = 0; u < kLLPieces; ++u) {
-        const int chunk = tid + u * (int)blockDim.x;
-        if (chunk < npieces) {
-            if (FP8) fp8_store(pf[u], chunk, H, k, my_slot, nrows, static_cast<uint8_t*>(recv), recv_sc);
-            else bf16_store(pb[u], chunk, H, k, my_slot, nrows, static_cast<uint16_t*>(recv));
-        }
+        if (u * nt >= npieces) break;
+        const int chunk = tid + u * nt;
+        if (FP8) fp8_store(pf[u], chunk, H, k, my_slot, nrows, static_cast<uint8_t*>(recv), recv_sc);
+        else bf16_store(pb[u], chunk, H, k, my_slot, nrows, static_cast<uint16_t*>(recv));
     }
 }
 

@@ -17,6 +17,12 @@ namespace ep {
 // code = e4m3_rne(x * inv).  x is read with default caching, the codes are
 // streamed (nt).  Loading and storing are separate steps so that a caller
 // can issue the loads before work the stores depend on.
+//
+// Every lane of the wave calls these, also lanes whose piece lies past the
+// end of the row: their loads read zeros and their payload stores are
+// dropped by the per-row buffer resources, and the one plain store (the
+// scale) is guarded per lane.  So the v_readlane of the row indices never
+// runs under a partial exec mask.
 struct Fp8Piece {
     i32x4 a, b;
 };
@@ -56,12 +62,13 @@ __device__ __forceinline__ void fp8_store(const Fp8Piece& v, int chunk, int H, i
     q.w = (int)pack_e4m3x4(f[12] * inv, f[13] * inv, f[14] * inv, f[15] * inv);
 
     const int nblk = H >> 7;
+    const bool sc_lane = (lane & 7) == 0 && chunk * 16 < H;  // first lane of a block inside the row
     for (int j = 0; j < k; ++j) {
         const int r = __builtin_amdgcn_readlane(my_slot, j);
         if ((unsigned)r < (unsigned)nrows) {
             const auto rr = buffer_rsrc(recv + (size_t)r * H, (uint32_t)H);
             __builtin_amdgcn_raw_buffer_store_b128(q, rr, chunk * 16, 0, kStream);
-            if ((lane & 7) == 0) recv_sc[(size_t)r * nblk + (chunk >> 3)] = sc;
+            if (sc_lane) recv_sc[(size_t)r * nblk + (chunk >> 3)] = sc;
         }
     }
 }
