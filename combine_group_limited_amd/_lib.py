@@ -2,13 +2,14 @@
 
 torch is imported first so that the HIP runtime torch ships is the one in
 the process; libep.so links libamdhip64.so.7 by SONAME and binds to it.
-If libep.so is missing it is built with hipcc; if it cannot be loaded the
-import fails: there is no fallback path.
+If libep.so is missing, or was built from other sources than the current
+ones (a content hash recorded at build time), it is rebuilt with hipcc, and
+without hipcc the load is refused; if it cannot be loaded the import fails:
+there is no fallback path.
 """
 from __future__ import annotations
 
 import ctypes
-import os
 import threading
 
 import torch  # noqa: F401  (loads torch's HIP runtime before libep.so)
@@ -73,7 +74,11 @@ def lib() -> ctypes.CDLL:
     with _lock:
         if _lib is not None:
             return _lib
-        if not os.path.exists(LIB_PATH):
+        if _build.is_stale():
+            if not _build.hipcc_available():
+                raise RuntimeError("%s is missing or was built from other sources than those in %s, "
+                                   "and hipcc is not available to rebuild it" % (LIB_PATH, _build.CSRC))
+            print("libep.so is missing or out of date: rebuilding", flush=True)
             _build.build()
         L = ctypes.CDLL(LIB_PATH)
         P = ctypes.c_void_p

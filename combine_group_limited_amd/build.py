@@ -5,6 +5,7 @@ Usage: python -m combine_group_limited_amd.build
 from __future__ import annotations
 
 import concurrent.futures as cf
+import hashlib
 import os
 import shutil
 import subprocess
@@ -16,6 +17,9 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(PKG, "_build")
 LIB_PATH = os.path.join(PKG, "libep.so")
+# content hash of the sources and flags the library was built from, written
+# next to it by build(); the loader compares it with the current sources
+HASH_PATH = LIB_PATH + ".sources"
 
 SOURCES = ["api.hip", "gate.hip", "layout.hip", "dispatch.hip", "combine.hip", "ll.hip"]
 HEADERS = ["device.h", "launch.h", "rows.h"]
@@ -45,11 +49,34 @@ def _inputs():
     return [os.path.join(CSRC, f) for f in SOURCES + HEADERS] + [os.path.join(INCLUDE, "ep.h")]
 
 
+def source_hash(inputs=None) -> str:
+    """SHA-256 over the compiler flags and the name and bytes of every input."""
+    h = hashlib.sha256("\0".join(HIPFLAGS).encode())
+    for p in (inputs if inputs is not None else _inputs()):
+        h.update(os.path.basename(p).encode() + b"\0")
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def built_hash():
+    """The source hash recorded when libep.so was built, or None."""
+    try:
+        with open(HASH_PATH) as f:
+            return f.read().strip()
+    except OSError:
+        return None
+
+
 def is_stale() -> bool:
-    if not os.path.exists(LIB_PATH):
-        return True
-    t = os.path.getmtime(LIB_PATH)
-    return any(os.path.getmtime(p) > t for p in _inputs())
+    """True when libep.so is missing or was built from other sources or
+    flags than the current ones (compared by content, not by time stamps,
+    which a copied tree need not keep)."""
+    return not os.path.exists(LIB_PATH) or built_hash() != source_hash()
+
+
+def hipcc_available() -> bool:
+    return os.path.exists(HIPCC) or shutil.which(HIPCC) is not None
 
 
 def _compile(src: str) -> str:
@@ -69,6 +96,7 @@ def _compile(src: str) -> str:
 def build(verbose: bool = False) -> str:
     """Compile every HIP source and link libep.so next to this file."""
     os.makedirs(BUILD_DIR, exist_ok=True)
+    digest = source_hash()
     srcs = [os.path.join(CSRC, f) for f in SOURCES]
     with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
         objs = list(ex.map(_compile, srcs))
@@ -78,6 +106,10 @@ def build(verbose: bool = False) -> str:
     if r.returncode != 0:
         raise RuntimeError("link failed:\n%s\n%s" % (" ".join(cmd), r.stderr))
     os.replace(tmp, LIB_PATH)
+    tmp = HASH_PATH + ".tmp%d" % os.getpid()
+    with open(tmp, "w") as f:
+        f.write(digest + "\n")
+    os.replace(tmp, HASH_PATH)
     if verbose:
         print("built", LIB_PATH)
     return LIB_PATH
