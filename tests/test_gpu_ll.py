@@ -139,29 +139,3 @@ def test_ll_route_on_gpu_end_to_end():
     oi, ow = oracle.route(lg, w.G, w.TG, w.k, w.topm)
     assert np.array_equal(to_host(idx), oi)
     check_ll(w, oi, ow, x, w.T, g)
-
-
-def test_calls_on_cu_range_streams_match_default_stream():
-    # the whole normal path and the low-latency path on streams confined to
-    # part of the GPU give the same bits as on the default stream
-    w = W.PREFILL.replace(T=512)
-    say("cu-range streams", w)
-    lg, x, y = W.gen_logits(w), W.gen_x(w), W.gen_y(w)
-    cfg = ep.Config.of(w)
-    ncu = torch.cuda.get_device_properties(0).multi_processor_count
-
-    def run(stream):
-        idx, wt = ep.route(cfg, to_dev(lg), stream=stream)
-        lay = ep.get_layout(cfg, idx, stream=stream)
-        recv, sc = ep.dispatch(cfg, to_dev(x, torch.bfloat16), lay["slot"], stream=stream)
-        out = ep.combine(cfg, to_dev(y, torch.bfloat16), lay["slot"], wt, stream=stream)
-        ll = ep.dispatch_ll(cfg, to_dev(x, torch.bfloat16), idx, 64, stream=stream)
-        torch.cuda.synchronize()
-        return [to_host(v) for v in (idx, wt, lay["slot"], recv, sc, out, ll["slot"], ll["count"])]
-
-    ref = run(None)
-    for first, num in ((0, 32), (ncu // 2, ncu // 2)):
-        with ep.CuRangeStream(first, num) as s:
-            got = run(s)
-        for a, b in zip(got, ref):
-            assert np.array_equal(a, b)
