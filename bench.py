@@ -112,7 +112,8 @@ def parse():
     ap.add_argument("--sets", type=int, default=0,
                     help="copies of all buffers used round-robin (0: enough for >= 2 GiB between reuses)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--cpu-seconds", type=float, default=16.0,
+                    help="CPU time of the oracle legs (half on one thread, half on all threads)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (for scaling HBM counters)")
     return ap.parse_args()
@@ -339,6 +340,7 @@ def run_normal(args, w):
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "fp32",
+        "storage_dtypes": {"dispatch": "fp8_e4m3 codes + fp32 scales" if fp8 else "bf16", "combine": "bf16"},
         "data": "synthetic",
         "config": {"workload": w.name, "path": "normal", "tokens": w.T, "hidden": w.H, "experts": w.E,
                    "groups": w.G, "topk_groups": w.TG, "topk": w.k, "virtual_ranks": w.R,
@@ -360,8 +362,17 @@ def run_normal(args, w):
     }
     dkey = "dispatch_fp8" if fp8 else "dispatch_bf16"
     rec["kernels"]["dispatch"]["traffic"] = _recorded_traffic(dkey, w.name)
-    if not args.no_cpu_baseline and fp8:
-        rec["cpu_baseline"] = cpu_baseline(w, lg_np, x_np, y_np, args.cpu_seconds)
+    rec["inputs"] = provenance(w, {"logits": lg_np, "x": x_np, "y": y_np})
+    if not args.no_cpu_baseline:
+        def to_host(t):
+            t = t.detach().cpu()
+            return t.view(torch.int16).numpy().view(np.uint16) if t.dtype == torch.bfloat16 else t.numpy()
+
+        gpu = {k: to_host(v) for k, v in sets[0].items()
+               if k in ("idx", "wt", "cnt", "ntok", "off", "slot", "recv_token", "recv", "scales", "out")}
+        rec["parity"], _, wt_o, lay_o = oracle_parity(w, fp8, gpu, lg_np, x_np, y_np)
+        del gpu
+        rec["cpu_baseline"] = cpu_baseline(w, fp8, x_np, y_np, wt_o, lay_o, args.cpu_seconds)
     return rec
 
 
@@ -756,32 +767,123 @@ def kernel_sha(kernel: str) -> str:
     return h.hexdigest()[:16]
 
 
-def cpu_baseline(w, lg, x, y, seconds: float):
-    """The CPU oracle (plain single-threaded C) on the same batch: route and
-    layout once, then FP8 dispatch + combine passes over the whole batch,
-    repeated until `seconds` of CPU time have elapsed (at most 64 passes)."""
+def host_cpu():
+    """CPU model and the threads this process may use (the machine's CPU share:
+    the smaller of the affinity set and OMP_NUM_THREADS when it is set)."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    avail = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else (os.cpu_count() or 1)
+    omp = os.environ.get("OMP_NUM_THREADS", "")
+    use = min(avail, int(omp)) if omp.isdigit() and int(omp) > 0 else avail
+    return {"cpu_model": model, "cpus_visible": os.cpu_count(), "cpus_affinity": avail, "threads": use}
+
+
+def provenance(w, arrays):
+    """Seeds and input hashes of the synthetic batch."""
+    import numpy as np
+
+    import workloads as W
+    return {"seed": w.seed, "generator": "numpy %s PCG64, SeedSequence(seed).spawn(4): x, logits, y, bias"
+            % np.__version__, "sha256": {k: W.sha256(v) for k, v in arrays.items()}}
+
+
+def oracle_parity(w, fp8, gpu, lg, x, y):
+    """The oracle's outputs on the bench's own batch against the GPU's
+    (buffer set 0 after the timed steps): bit-exact for every integer output,
+    the weights, payload and scales; combine counted in bf16 ulps.  Returns
+    (parity record, the oracle's route and layout for the timing legs)."""
     import numpy as np
 
     import oracle
 
+    def ordinal(b):  # bf16 patterns -> integers monotone in value, +0 and -0 both 0
+        b = np.asarray(b, dtype=np.uint16).astype(np.int64)
+        return np.where(b & 0x8000, -(b & 0x7FFF), b & 0x7FFF)
+
     idx, wt = oracle.route(lg, w.G, w.TG, w.k, w.topm)
     lay = oracle.layout(idx, w.E, w.R)
-    q = np.empty((w.nrows, w.H), np.uint8)
+    checks = {"idx": (gpu["idx"], idx), "w": (gpu["wt"].view(np.uint32), wt.view(np.uint32)),
+              "cnt": (gpu["cnt"], lay["cnt"]), "off": (gpu["off"], lay["off"]),
+              "ntok_rank": (gpu["ntok"], lay["ntok_rank"]), "slot": (gpu["slot"], lay["slot"]),
+              "recv_token": (gpu["recv_token"], lay["recv_token"])}
+    if fp8:
+        q, sc = oracle.dispatch_fp8(x, lay["slot"], w.nrows)
+        checks["payload"] = (gpu["recv"], q)
+        checks["scales"] = (gpu["scales"].view(np.uint32), sc.view(np.uint32))
+    else:
+        checks["payload"] = (gpu["recv"], oracle.dispatch_bf16(x, lay["slot"], w.nrows))
+    rec = {}
+    for k, (g, o) in checks.items():
+        n = int(np.count_nonzero(np.asarray(g).ravel() != np.asarray(o).ravel()))
+        rec[k] = "bit-exact" if n == 0 else "%d of %d differ" % (n, np.asarray(o).size)
+    d = np.abs(ordinal(gpu["out"]) - ordinal(oracle.combine(y, lay["slot"], wt)))
+    rec["combine_max_ulp"] = int(d.max()) if d.size else 0
+    rec["combine_elements_differing"] = int((d > 0).sum())
+    ok = all(v == "bit-exact" for k, v in rec.items() if not k.startswith("combine")) and rec["combine_max_ulp"] <= 1
+    rec["verdict"] = "pass" if ok else "FAIL"
+    rec["bar"] = "bit-exact routing, weights, layout, payload and scales; combine within 1 bf16 ulp"
+    return rec, idx, wt, lay
+
+
+def cpu_baseline(w, fp8, x, y, wt, lay, seconds: float):
+    """The CPU oracle (plain single-threaded C, unchanged) timed on the same
+    batch: dispatch + combine passes over the whole batch, on one thread and
+    on every thread the host gives this process (the oracle's own functions
+    called on token slices from a thread pool; ctypes releases the GIL).
+    Each leg repeats passes for about half of `seconds`."""
+    import concurrent.futures as cf
+
+    import numpy as np
+
+    import oracle
+
+    q = np.empty((w.nrows, w.H), np.uint8 if fp8 else np.uint16)
     sc = np.empty((w.nrows, w.H // 128), np.float32)
-    times = []
-    t_start = time.perf_counter()
-    while True:
-        t0 = time.perf_counter()
-        oracle.dispatch_fp8(x, lay["slot"], w.nrows, q, sc)
-        oracle.combine(y, lay["slot"], wt)
-        times.append(time.perf_counter() - t0)
-        if time.perf_counter() - t_start >= seconds or len(times) >= 64:
-            break
-    t = float(np.median(times))
-    return {"value": round((w.bytes_dispatch_fp8() + w.bytes_combine()) / t / 1e9, 4), "unit": "GB/s",
-            "cores": 1, "kind": "oracle",
-            "sample": "full %s batch (%d tokens), FP8 dispatch + combine, median of %d passes, %.2f s each"
-                      % (w.name, w.T, len(times), t)}
+    out = np.empty((w.T, w.H), np.uint16)
+    slot = lay["slot"]
+    nbytes = (w.bytes_dispatch_fp8() if fp8 else w.bytes_dispatch_bf16()) + w.bytes_combine()
+
+    def part(t0, t1):
+        if fp8:
+            oracle.dispatch_fp8(x[t0:t1], slot[t0:t1], w.nrows, q, sc)
+        else:
+            oracle.dispatch_bf16(x[t0:t1], slot[t0:t1], w.nrows, q)
+        out[t0:t1] = oracle.combine(y, slot[t0:t1], wt[t0:t1])
+
+    def leg(threads):
+        times = []
+        t_start = time.perf_counter()
+        with cf.ThreadPoolExecutor(max_workers=threads) as pool:
+            cuts = np.linspace(0, w.T, 4 * threads + 1).astype(int) if threads > 1 else np.array([0, w.T])
+            while True:
+                t0 = time.perf_counter()
+                if threads == 1:
+                    part(0, w.T)
+                else:
+                    list(pool.map(lambda i: part(cuts[i], cuts[i + 1]), range(len(cuts) - 1)))
+                times.append(time.perf_counter() - t0)
+                if time.perf_counter() - t_start >= seconds / 2 or len(times) >= 64:
+                    break
+        t = float(np.median(times))
+        return round(nbytes / t / 1e9, 4), t, len(times)
+
+    host = host_cpu()
+    one, t1, n1 = leg(1)
+    many, tn, nn = leg(host["threads"])
+    kind = "FP8" if fp8 else "BF16"
+    return {"value": many, "unit": "GB/s", "cores": host["threads"], "kind": "oracle",
+            "sample": "full %s batch (%d tokens), %s dispatch + combine, median of %d passes of %.3f s on %d "
+                      "threads (token slices)" % (w.name, w.T, kind, nn, tn, host["threads"]),
+            "one_thread": {"value": one, "unit": "GB/s", "cores": 1,
+                           "sample": "median of %d passes of %.3f s" % (n1, t1)},
+            "host": host, "speedup_vs_one_thread": round(many / one, 2)}
 
 
 if __name__ == "__main__":

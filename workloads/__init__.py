@@ -146,4 +146,5 @@ def gen_y(w: Workload, nrows: int | None = None, chunk_rows: int = 8192) -> np.n
 
 
 def sha256(a: np.ndarray) -> str:
-    return hashlib.sha256(np.ascontiguousarray(a).tobytes()).hexdigest()[:16]
+    """SHA-256 of an array's bytes in C order (hex digest)."""
+    return hashlib.sha256(memoryview(np.ascontiguousarray(a)).cast("B")).hexdigest()
