@@ -5,6 +5,14 @@ Argument marshalling only: shapes, dtypes, devices and contiguity are
 checked here (the C ABI sees bare pointers and cannot), outputs are
 allocated with torch.empty when not given, and every computation runs in
 libep.so's kernels on the caller's current stream (or `stream`).
+
+With an explicit `stream` that is not torch's current stream, the caller
+keeps every tensor a call reads or returns alive until the work on that
+stream has finished (for example until a synchronisation), as the C ABI
+requires: torch's caching allocator only orders reuse of freed memory on
+the current stream.  (Tensor.record_stream is no substitute for streams the
+caller destroys, such as CuRangeStream: the allocator would later record
+events on the destroyed stream.)
 """
 from __future__ import annotations
 
@@ -66,20 +74,6 @@ def _ptr(t) -> int:
     return 0 if t is None else t.data_ptr()
 
 
-def _hold(stream, *tensors) -> None:
-    """For work enqueued on an explicit stream: record that stream on every
-    tensor the call reads or writes, so that torch's caching allocator does
-    not hand their memory out again (to work on another stream) before the
-    kernels on `stream` have run.  Nothing to do on the current stream."""
-    if stream is None:
-        return
-    ts = stream if isinstance(stream, torch.cuda.Stream) else getattr(stream, "torch", None)
-    if ts is None:
-        return
-    for t in tensors:
-        if isinstance(t, torch.Tensor):
-            t.record_stream(ts)
-
 
 def _want(t: torch.Tensor, name: str, shape, dtype, device) -> None:
     if not isinstance(t, torch.Tensor):
@@ -110,7 +104,6 @@ def route(cfg: Config, logits: torch.Tensor, topk_idx=None, topk_w=None, stream=
     _want(topk_idx, "topk_idx", (cfg.T, cfg.k), torch.int32, dev)
     _want(topk_w, "topk_w", (cfg.T, cfg.k), torch.float32, dev)
     c = cfg.c()
-    _hold(stream, logits, topk_idx, topk_w)
     _check(L.lib().ep_route(ctypes.byref(c), _ptr(logits), _ptr(topk_idx), _ptr(topk_w),
                             _stream(stream, dev)), "ep_route")
     return topk_idx, topk_w
@@ -125,7 +118,6 @@ def scores(cfg: Config, logits: torch.Tensor, out=None, stream=None) -> torch.Te
         out = torch.empty((cfg.T, cfg.E), dtype=torch.float32, device=dev)
     _want(out, "scores", (cfg.T, cfg.E), torch.float32, dev)
     c = cfg.c()
-    _hold(stream, logits, out)
     _check(L.lib().ep_scores(ctypes.byref(c), _ptr(logits), _ptr(out), _stream(stream, dev)), "ep_scores")
     return out
 
@@ -162,7 +154,6 @@ def get_layout(cfg: Config, topk_idx: torch.Tensor, out: dict | None = None, wor
     if workspace.dtype != torch.uint8 or workspace.device != dev or not workspace.is_contiguous():
         raise ValueError("workspace must be a contiguous uint8 tensor on %s" % dev)
     c = cfg.c()
-    _hold(stream, topk_idx, workspace, *o.values())
     _check(L.lib().ep_get_layout(ctypes.byref(c), _ptr(topk_idx), _ptr(o["cnt"]), _ptr(o["ntok_rank"]),
                                  _ptr(o["off"]), _ptr(o["slot"]), _ptr(rt), _ptr(workspace),
                                  workspace.numel(), _stream(stream, dev)), "ep_get_layout")
@@ -199,7 +190,6 @@ def dispatch(cfg: Config, x: torch.Tensor, slot: torch.Tensor, recv_dtype: str =
     else:
         raise ValueError("recv_dtype must be 'fp8' or 'bf16'")
     c = cfg.c()
-    _hold(stream, x, slot, recv, recv_scales)
     _check(L.lib().ep_dispatch(ctypes.byref(c), _ptr(x), _ptr(slot), code, _ptr(recv), _ptr(recv_scales),
                                _stream(stream, dev)), "ep_dispatch")
     return recv, recv_scales
@@ -215,7 +205,6 @@ def combine(cfg: Config, y: torch.Tensor, slot: torch.Tensor, topk_w: torch.Tens
         out = torch.empty((cfg.T, cfg.H), dtype=torch.bfloat16, device=dev)
     _want(out, "out", (cfg.T, cfg.H), torch.bfloat16, dev)
     c = cfg.c()
-    _hold(stream, y, slot, topk_w, out)
     _check(L.lib().ep_combine(ctypes.byref(c), _ptr(y), _ptr(slot), _ptr(topk_w), _ptr(out),
                               _stream(stream, dev)), "ep_combine")
     return out
@@ -262,7 +251,6 @@ def dispatch_ll(cfg: Config, x: torch.Tensor, topk_idx: torch.Tensor, capacity: 
     _want(recv_src, "recv_src", (nrows,), torch.int32, dev)
     _want(slot, "slot", (cfg.T, cfg.k), torch.int32, dev)
     c = cfg.c()
-    _hold(stream, x, topk_idx, recv, recv_scales, recv_count, recv_src, slot)
     _check(L.lib().ep_dispatch_ll(ctypes.byref(c), _ptr(x), _ptr(topk_idx), capacity, code, _ptr(recv),
                                   _ptr(recv_scales), _ptr(recv_count), _ptr(recv_src), _ptr(slot),
                                   _stream(stream, dev)), "ep_dispatch_ll")
@@ -281,7 +269,6 @@ def combine_ll(cfg: Config, capacity: int, y: torch.Tensor, slot: torch.Tensor, 
         out = torch.empty((cfg.T, cfg.H), dtype=torch.bfloat16, device=dev)
     _want(out, "out", (cfg.T, cfg.H), torch.bfloat16, dev)
     c = cfg.c()
-    _hold(stream, y, slot, topk_w, out)
     _check(L.lib().ep_combine_ll(ctypes.byref(c), capacity, _ptr(y), _ptr(slot), _ptr(topk_w), _ptr(out),
                                  _stream(stream, dev)), "ep_combine_ll")
     return out
@@ -319,7 +306,6 @@ def get_rank_layout(cfg: Config, topk_idx: torch.Tensor, out: dict | None = None
     if workspace.dtype != torch.uint8 or workspace.device != dev or not workspace.is_contiguous():
         raise ValueError("workspace must be a contiguous uint8 tensor on %s" % dev)
     c = cfg.c()
-    _hold(stream, topk_idx, workspace, *o.values())
     _check(L.lib().ep_get_rank_layout(ctypes.byref(c), _ptr(topk_idx), _ptr(o["rank_count"]), _ptr(o["rank_offset"]),
                                       _ptr(o["rank_slot"]), _ptr(rt), _ptr(workspace), workspace.numel(),
                                       _stream(stream, dev)), "ep_get_rank_layout")
@@ -339,7 +325,6 @@ def combine_rank_partial(cfg: Config, y: torch.Tensor, topk_idx: torch.Tensor, s
         partial = torch.empty((cfg.nrows, cfg.H), dtype=torch.bfloat16, device=dev)
     _want(partial, "partial", (cfg.nrows, cfg.H), torch.bfloat16, dev)
     c = cfg.c()
-    _hold(stream, y, topk_idx, slot, topk_w, rank_slot, partial)
     _check(L.lib().ep_combine_rank_partial(ctypes.byref(c), _ptr(y), _ptr(topk_idx), _ptr(slot), _ptr(topk_w),
                                            _ptr(rank_slot), _ptr(partial), _stream(stream, dev)),
            "ep_combine_rank_partial")
@@ -355,7 +340,6 @@ def combine_ranks(cfg: Config, partial: torch.Tensor, rank_slot: torch.Tensor, o
         out = torch.empty((cfg.T, cfg.H), dtype=torch.bfloat16, device=dev)
     _want(out, "out", (cfg.T, cfg.H), torch.bfloat16, dev)
     c = cfg.c()
-    _hold(stream, partial, rank_slot, out)
     _check(L.lib().ep_combine_ranks(ctypes.byref(c), _ptr(partial), _ptr(rank_slot), _ptr(out),
                                     _stream(stream, dev)), "ep_combine_ranks")
     return out
