@@ -15,6 +15,7 @@ from .api import (  # noqa: F401
     dispatch,
     dispatch_ll,
     get_layout,
+    get_layout_static,
     get_rank_layout,
     layout_workspace_bytes,
     rank_layout_workspace_bytes,

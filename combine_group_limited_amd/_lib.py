@@ -24,6 +24,10 @@ EP_ERR_ALIGNMENT = -2
 EP_ERR_UNSUPPORTED = -3
 EP_ERR_WORKSPACE = -4
 EP_ERR_HIP = -5
+EP_ERR_SCRATCH_LIMIT = -6
+
+# bytes of the device array ep_get_layout_static uses as its scratch
+EP_STATIC_SCRATCH_BYTES = 1 << 20
 
 EP_RECV_FP8_E4M3 = 0
 EP_RECV_BF16 = 1
@@ -38,6 +42,7 @@ EXPORTS = (
     "ep_scores",
     "ep_layout_workspace_bytes",
     "ep_get_layout",
+    "ep_get_layout_static",
     "ep_dispatch",
     "ep_combine",
     "ep_dispatch_ll",
@@ -100,6 +105,8 @@ def lib() -> ctypes.CDLL:
         L.ep_layout_workspace_bytes.restype = ctypes.c_size_t
         L.ep_get_layout.argtypes = [C, P, P, P, P, P, P, P, ctypes.c_size_t, P]
         L.ep_get_layout.restype = I
+        L.ep_get_layout_static.argtypes = [C, P, P, P, P, P, P, P]
+        L.ep_get_layout_static.restype = I
         L.ep_dispatch.argtypes = [C, P, P, I, P, P, P]
         L.ep_dispatch.restype = I
         L.ep_combine.argtypes = [C, P, P, P, P, P]

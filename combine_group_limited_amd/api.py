@@ -160,6 +160,36 @@ def get_layout(cfg: Config, topk_idx: torch.Tensor, out: dict | None = None, wor
     return o
 
 
+def get_layout_static(cfg: Config, topk_idx: torch.Tensor, out: dict | None = None,
+                      with_recv_token: bool = True, stream=None) -> dict:
+    """get_layout without a workspace: the library's static device scratch
+    (at most EP_STATIC_SCRATCH_BYTES) stands in for it, so the call
+    allocates nothing when `out` holds every output.  Calls that may overlap
+    on one GPU race on that scratch."""
+    dev = topk_idx.device
+    _want(topk_idx, "topk_idx", (cfg.T, cfg.k), torch.int32, None)
+    o = dict(out or {})
+    i32 = dict(dtype=torch.int32, device=dev)
+    o.setdefault("cnt", torch.empty(cfg.E, **i32))
+    o.setdefault("ntok_rank", torch.empty(cfg.R, **i32))
+    o.setdefault("off", torch.empty(cfg.E + 1, **i32))
+    o.setdefault("slot", torch.empty((cfg.T, cfg.k), **i32))
+    if with_recv_token:
+        o.setdefault("recv_token", torch.empty(cfg.T * cfg.k, **i32))
+    _want(o["cnt"], "cnt", (cfg.E,), torch.int32, dev)
+    _want(o["ntok_rank"], "ntok_rank", (cfg.R,), torch.int32, dev)
+    _want(o["off"], "off", (cfg.E + 1,), torch.int32, dev)
+    _want(o["slot"], "slot", (cfg.T, cfg.k), torch.int32, dev)
+    rt = o.get("recv_token")
+    if rt is not None:
+        _want(rt, "recv_token", (cfg.T * cfg.k,), torch.int32, dev)
+    c = cfg.c()
+    _check(L.lib().ep_get_layout_static(ctypes.byref(c), _ptr(topk_idx), _ptr(o["cnt"]), _ptr(o["ntok_rank"]),
+                                        _ptr(o["off"]), _ptr(o["slot"]), _ptr(rt), _stream(stream, dev)),
+           "ep_get_layout_static")
+    return o
+
+
 def dispatch(cfg: Config, x: torch.Tensor, slot: torch.Tensor, recv_dtype: str = "fp8", recv=None,
              recv_scales=None, stream=None):
     """Dispatch bf16 x [T, H] to T*k receive rows.  fp8: returns (recv uint8

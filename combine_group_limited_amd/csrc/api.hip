@@ -3,14 +3,43 @@
 // here allocates or synchronises.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <stdint.h>
 
 #include "ep.h"
 #include "launch.h"
 
+// Layout scratch of ep_get_layout_static.  In host code `scratch` names a
+// host-side stand-in, not the device array: kernels get the array's device
+// address, looked up once per device (hipGetSymbolAddress, with that device
+// current) and kept in g_scratch_dev.
+static __device__ __align__(256) unsigned char scratch[EP_STATIC_SCRATCH_BYTES];
+
 namespace {
 
 thread_local int g_last_hip_error = 0;
+
+constexpr int kMaxDevices = 256;
+std::atomic<void*> g_scratch_dev[kMaxDevices];
+
+// Device address of `scratch` on the current device (nullptr with the
+// hipError_t in *err on failure).  Two threads racing on a device's first
+// call both look it up and store the same address.
+void* static_scratch(hipError_t* err) {
+    int dev = 0;
+    *err = hipGetDevice(&dev);
+    if (*err != hipSuccess) return nullptr;
+    if (dev < 0 || dev >= kMaxDevices) {
+        *err = hipErrorInvalidDevice;
+        return nullptr;
+    }
+    void* p = g_scratch_dev[dev].load(std::memory_order_acquire);
+    if (p) return p;
+    *err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (*err != hipSuccess) return nullptr;
+    g_scratch_dev[dev].store(p, std::memory_order_release);
+    return p;
+}
 
 constexpr int32_t kMaxTokens = 1 << 24;
 constexpr int32_t kMaxHidden = 16384;
@@ -79,6 +108,9 @@ EP_API const char* ep_strerror(int code) {
         case EP_ERR_UNSUPPORTED: return "configuration outside the kernels' supported limits";
         case EP_ERR_WORKSPACE: return "workspace missing or too small";
         case EP_ERR_HIP: return "HIP kernel launch failed (see ep_last_hip_error)";
+        case EP_ERR_SCRATCH_LIMIT:
+            return "layout needs more scratch than the library's static array (EP_STATIC_SCRATCH_BYTES); "
+                   "use ep_get_layout with a workspace";
         default: return "unknown error code";
     }
 }
@@ -126,6 +158,28 @@ EP_API int ep_get_layout(const ep_config_t* cfg, const int32_t* topk_idx, int32_
     if (!aligned(workspace, 16)) return EP_ERR_ALIGNMENT;
     return hip_status(ep::launch_layout(s, topk_idx, cnt_expert, ntok_rank, expert_offset, slot, recv_token,
                                         workspace, static_cast<hipStream_t>(stream)));
+}
+
+EP_API int ep_get_layout_static(const ep_config_t* cfg, const int32_t* topk_idx, int32_t* cnt_expert,
+                                int32_t* ntok_rank, int32_t* expert_offset, int32_t* slot, int32_t* recv_token,
+                                void* stream) {
+    int rc = validate(cfg);
+    if (rc) return rc;
+    if (!cnt_expert || !ntok_rank || !expert_offset) return EP_ERR_INVALID_ARG;
+    if (cfg->num_tokens > 0 && (!topk_idx || !slot)) return EP_ERR_INVALID_ARG;
+    if (!aligned(topk_idx, 4) || !aligned(cnt_expert, 4) || !aligned(ntok_rank, 4) ||
+        !aligned(expert_offset, 4) || !aligned(slot, 4) || !aligned(recv_token, 4))
+        return EP_ERR_ALIGNMENT;
+    const ep::Shape s = shape_of(cfg);
+    if (ep::layout_workspace_bytes(s) > EP_STATIC_SCRATCH_BYTES) return EP_ERR_SCRATCH_LIMIT;
+    hipError_t e = hipSuccess;
+    void* ws = static_scratch(&e);
+    if (!ws) {
+        (void)hipGetLastError();  // returned here, not left pending for the next call
+        return hip_status(e);
+    }
+    return hip_status(ep::launch_layout(s, topk_idx, cnt_expert, ntok_rank, expert_offset, slot, recv_token, ws,
+                                        static_cast<hipStream_t>(stream)));
 }
 
 EP_API int ep_dispatch(const ep_config_t* cfg, const void* x, const int32_t* slot, int recv_dtype, void* recv,

@@ -57,7 +57,7 @@ extern "C" {
 
 #define EP_API __attribute__((visibility("default")))
 
-#define EP_ABI_VERSION 2
+#define EP_ABI_VERSION 3
 
 /* Return codes */
 #define EP_OK               0
@@ -66,6 +66,7 @@ extern "C" {
 #define EP_ERR_UNSUPPORTED (-3)  /* valid, but outside the kernels' limits */
 #define EP_ERR_WORKSPACE   (-4)  /* workspace missing or too small         */
 #define EP_ERR_HIP         (-5)  /* a kernel launch failed                 */
+#define EP_ERR_SCRATCH_LIMIT (-6) /* needs more than the static scratch     */
 
 /* Receive payload types for ep_dispatch */
 #define EP_RECV_FP8_E4M3 0
@@ -165,6 +166,33 @@ EP_API int ep_get_layout(const ep_config_t* cfg, const int32_t* topk_idx,
                          int32_t* expert_offset, int32_t* slot,
                          int32_t* recv_token, void* workspace,
                          size_t workspace_bytes, void* stream);
+
+/* Bytes of the device array ep_get_layout_static uses as its scratch. */
+#define EP_STATIC_SCRATCH_BYTES (1u << 20)
+
+/* ep_get_layout without a workspace argument and without any allocation,
+ * for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation).  The
+ * scratch ep_get_layout takes as `workspace` (ep_layout_workspace_bytes(cfg)
+ * bytes) is instead a file-scope device array of EP_STATIC_SCRATCH_BYTES,
+ * which the library holds on every GPU it runs on until the process ends;
+ * its address on a device is looked up (hipGetSymbolAddress) on the first
+ * call on that device and kept.  Arguments, results, determinism and
+ * alignment as ep_get_layout.
+ * Errors: as ep_get_layout, plus EP_ERR_SCRATCH_LIMIT, before any HIP call,
+ * when ep_layout_workspace_bytes(cfg) > EP_STATIC_SCRATCH_BYTES (with 256
+ * experts and 32 ranks: more than about 466,000 routed pairs; use
+ * ep_get_layout then), and EP_ERR_HIP when the current device or the
+ * array's address cannot be obtained.
+ * Every call on one GPU uses that GPU's one array: calls whose work may
+ * overlap on one GPU (streams not ordered with each other, or several host
+ * threads) race, and the caller must serialise them.  The array keeps the
+ * last call's contents; a call reads only scratch words it has written
+ * first, so nothing needs clearing. */
+EP_API int ep_get_layout_static(const ep_config_t* cfg, const int32_t* topk_idx,
+                                int32_t* cnt_expert, int32_t* ntok_rank,
+                                int32_t* expert_offset, int32_t* slot,
+                                int32_t* recv_token, void* stream);
 
 /* Dispatch ([DAY2] "DeepEP是什么"; FP8 payload: [NEWS] "具体性能方面",
  * [DAY2] "DeepEP的关键技术").

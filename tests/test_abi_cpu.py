@@ -29,8 +29,8 @@ def test_every_declared_function_is_exported():
 
 def test_version_and_messages():
     lib = ep.lib()
-    assert lib.ep_abi_version() == 2
-    for code in (0, -1, -2, -3, -4, -5, 42):
+    assert lib.ep_abi_version() == 3
+    for code in (0, -1, -2, -3, -4, -5, -6, 42):
         assert len(lib.ep_strerror(code)) > 0
     assert lib.ep_last_hip_error() == 0
 
@@ -125,6 +125,30 @@ def test_layout_rejections():
                              None) == L.EP_ERR_INVALID_ARG
     assert lib.ep_get_layout(ctypes.byref(c), FAKE, FAKE, FAKE, FAKE, FAKE + 1, FAKE, FAKE, need,
                              None) == L.EP_ERR_ALIGNMENT
+
+
+def test_layout_static_rejections():
+    # validated before any HIP call, so fake device addresses are safe here
+    lib = ep.lib()
+    c = _cfg().c()
+    assert lib.ep_layout_workspace_bytes(ctypes.byref(c)) <= L.EP_STATIC_SCRATCH_BYTES
+    args = [FAKE] * 6
+    assert lib.ep_get_layout_static(None, *args, None) == L.EP_ERR_INVALID_ARG
+    assert lib.ep_get_layout_static(ctypes.byref(c), FAKE, None, FAKE, FAKE, FAKE, FAKE,
+                                    None) == L.EP_ERR_INVALID_ARG
+    assert lib.ep_get_layout_static(ctypes.byref(c), FAKE, FAKE, FAKE, FAKE, FAKE + 2, FAKE,
+                                    None) == L.EP_ERR_ALIGNMENT
+    # beyond the static scratch: the largest T whose workspace fits passes
+    # validation of the size, one more count block does not
+    E, R, k = 256, 32, 8
+    fits = (L.EP_STATIC_SCRATCH_BYTES // (4 * (E + R))) * 512 // k
+    big = _cfg(T=fits + 512 // k).c()
+    assert lib.ep_layout_workspace_bytes(ctypes.byref(big)) > L.EP_STATIC_SCRATCH_BYTES
+    assert lib.ep_get_layout_static(ctypes.byref(big), *args, None) == L.EP_ERR_SCRATCH_LIMIT
+    msg = lib.ep_strerror(L.EP_ERR_SCRATCH_LIMIT).decode()
+    assert "ep_get_layout" in msg and "scratch" in msg
+    ok = _cfg(T=fits).c()
+    assert lib.ep_layout_workspace_bytes(ctypes.byref(ok)) <= L.EP_STATIC_SCRATCH_BYTES
 
 
 def test_dispatch_rejections():
