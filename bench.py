@@ -2,8 +2,8 @@
 """Benchmark of the MoE routing -> FP8 dispatch -> BF16 combine path on one
 MI355X.
 
-One step = ep_route + ep_get_layout + ep_dispatch (FP8 E4M3, 1x128 scales)
-+ ep_combine over one batch of seeded synthetic input already resident in
+One step = ep_route_layout (routing and layout) + ep_dispatch (FP8 E4M3,
+1x128 scales) + ep_combine over one batch of seeded synthetic input already resident in
 HBM (4096 tokens x 7168 hidden, 256 experts in 8 groups, top-4 groups,
 top-8 experts, 32 virtual ranks by default).  Expert outputs for the combine
 are a resident synthetic buffer (the expert computation is not part of the
@@ -102,7 +102,7 @@ def parse():
     ap.add_argument("--config", default=None,
                     help="workload (default: prefill for the normal path, decode for the low-latency path)")
     ap.add_argument("--path", choices=("normal", "ll", "overlap", "dedup"), default="normal",
-                    help="normal: route + layout + dispatch + combine; ll: route + dispatch_ll + combine_ll; "
+                    help="normal: route_layout + dispatch + combine; ll: route + dispatch_ll + combine_ll; "
                          "overlap: dispatch + combine on a CU budget next to a bf16 GEMM on the other CUs; "
                          "dedup: per-rank deduplicated dispatch + in-rank partial combine + combine of partials")
     ap.add_argument("--cus", default="16,24,32,64,128", help="CU budgets of the overlap path")
@@ -191,9 +191,8 @@ def timed_steps(args, nsets, launch_stages, stages):
 
 def launch_step(lib, cp, p, code, ws, nws, sh, check):
     """One step of the normal path on stream handle `sh`, no events."""
-    check(lib.ep_route(cp, p["logits"], p["idx"], p["wt"], sh), "ep_route")
-    check(lib.ep_get_layout(cp, p["idx"], p["cnt"], p["ntok"], p["off"], p["slot"], p["recv_token"],
-                            ws.data_ptr(), nws, sh), "ep_get_layout")
+    check(lib.ep_route_layout(cp, p["logits"], p["idx"], p["wt"], p["cnt"], p["ntok"], p["off"], p["slot"],
+                              p["recv_token"], ws.data_ptr(), nws, sh), "ep_route_layout")
     check(lib.ep_dispatch(cp, p["x"], p["slot"], code, p["recv"], p["scales"], sh), "ep_dispatch")
     check(lib.ep_combine(cp, p["y"], p["slot"], p["wt"], p["out"], sh), "ep_combine")
 
@@ -245,7 +244,7 @@ def kernel_table(dur, bytes_):
 
 
 def run_normal(args, w):
-    """route + layout + dispatch + combine on resident buffers."""
+    """route_layout (routing and layout) + dispatch + combine on resident buffers."""
     import numpy as np
     import torch
 
@@ -256,7 +255,7 @@ def run_normal(args, w):
     cfg = ep.Config.of(w)
     dev = torch.device("cuda", 0)
     fp8 = args.recv_dtype == "fp8"
-    bytes_ = dict(route=w.bytes_route(), layout=w.bytes_layout(),
+    bytes_ = dict(route_layout=w.bytes_route() + w.bytes_layout(),
                   dispatch=w.bytes_dispatch_fp8() if fp8 else w.bytes_dispatch_bf16(), combine=w.bytes_combine())
     touched = sum(bytes_.values())
     nsets = buffer_sets(args.sets, touched, touched)
@@ -268,7 +267,7 @@ def run_normal(args, w):
     x0 = torch.from_numpy(x_np.view(np.int16)).view(torch.bfloat16).to(dev)
     y0 = torch.from_numpy(y_np.view(np.int16)).view(torch.bfloat16).to(dev)
     i32 = dict(dtype=torch.int32, device=dev)
-    ws = torch.empty(max(16, ep.layout_workspace_bytes(cfg)), dtype=torch.uint8, device=dev)
+    ws = torch.empty(max(16, ep.route_layout_workspace_bytes(cfg)), dtype=torch.uint8, device=dev)
     sets = []
     for i in range(nsets):
         sets.append(dict(
@@ -285,9 +284,8 @@ def run_normal(args, w):
 
     # validate once through the checked binding, then call the C ABI directly
     for b in sets:
-        ep.route(cfg, b["logits"], b["idx"], b["wt"])
-        ep.get_layout(cfg, b["idx"], dict(cnt=b["cnt"], ntok_rank=b["ntok"], off=b["off"], slot=b["slot"],
-                                          recv_token=b["recv_token"]), ws)
+        ep.route_layout(cfg, b["logits"], dict(idx=b["idx"], w=b["wt"], cnt=b["cnt"], ntok_rank=b["ntok"],
+                                               off=b["off"], slot=b["slot"], recv_token=b["recv_token"]), ws)
         ep.dispatch(cfg, b["x"], b["slot"], args.recv_dtype, b["recv"], b["scales"])
         ep.combine(cfg, b["y"], b["slot"], b["wt"], b["out"])
     torch.cuda.synchronize()
@@ -306,17 +304,15 @@ def run_normal(args, w):
     def launch(i, rec):
         p = ptr[i]
         rec(0)
-        check(lib.ep_route(cp, p["logits"], p["idx"], p["wt"], sh), "ep_route")
+        check(lib.ep_route_layout(cp, p["logits"], p["idx"], p["wt"], p["cnt"], p["ntok"], p["off"], p["slot"],
+                                  p["recv_token"], ws.data_ptr(), nws, sh), "ep_route_layout")
         rec(1)
-        check(lib.ep_get_layout(cp, p["idx"], p["cnt"], p["ntok"], p["off"], p["slot"], p["recv_token"],
-                                ws.data_ptr(), nws, sh), "ep_get_layout")
-        rec(2)
         check(lib.ep_dispatch(cp, p["x"], p["slot"], code, p["recv"], p["scales"], sh), "ep_dispatch")
-        rec(3)
+        rec(2)
         check(lib.ep_combine(cp, p["y"], p["slot"], p["wt"], p["out"], sh), "ep_combine")
-        rec(4)
+        rec(3)
 
-    stages = ("route", "layout", "dispatch", "combine")
+    stages = ("route_layout", "dispatch", "combine")
     dur, wall = timed_steps(args, nsets, launch, stages)
     kt = kernel_table(dur, bytes_)
     graph_us = graph_step_us(args, nsets, lambda i, sh: launch_step(lib, cp, ptr[i], code, ws, nws, sh, check))
@@ -596,7 +592,7 @@ def run_overlap(args, w):
 
 
 def run_dedup(args, w):
-    """route + layout + rank layout + deduplicated FP8 dispatch (one row per
+    """route_layout + rank layout + deduplicated FP8 dispatch (one row per
     (token, rank)) + in-rank partial combine + combine of the partial rows,
     on resident buffers."""
     import numpy as np
@@ -616,7 +612,7 @@ def run_dedup(args, w):
     # the library's own rank layout
     c_idx, _ = ep.route(cfg, logits0)
     rows = int(ep.get_rank_layout(cfg, c_idx, with_rank_token=False)["rank_offset"][-1].item())
-    bytes_ = dict(route=w.bytes_route(), layout=w.bytes_layout(),
+    bytes_ = dict(route_layout=w.bytes_route() + w.bytes_layout(),
                   rank_layout=P * 8 + 4 * (2 * w.R + 1),
                   dispatch=w.T * 2 * w.H + rows * (w.H + 4 * B) + 4 * P,
                   partial=2 * w.H * P + 2 * w.H * rows + 16 * P,
@@ -626,7 +622,7 @@ def run_dedup(args, w):
     x0 = torch.from_numpy(x_np.view(np.int16)).view(torch.bfloat16).to(dev)
     y0 = torch.from_numpy(y_np.view(np.int16)).view(torch.bfloat16).to(dev)
     i32 = dict(dtype=torch.int32, device=dev)
-    ws = torch.empty(max(256, ep.layout_workspace_bytes(cfg)), dtype=torch.uint8, device=dev)
+    ws = torch.empty(max(256, ep.route_layout_workspace_bytes(cfg)), dtype=torch.uint8, device=dev)
     rws = torch.empty(max(256, ep.rank_layout_workspace_bytes(cfg)), dtype=torch.uint8, device=dev)
     sets = []
     for i in range(nsets):
@@ -642,9 +638,8 @@ def run_dedup(args, w):
             partial=torch.empty((P, w.H), dtype=torch.bfloat16, device=dev),
             out=torch.empty((w.T, w.H), dtype=torch.bfloat16, device=dev)))
     for b in sets:
-        ep.route(cfg, b["logits"], b["idx"], b["wt"])
-        ep.get_layout(cfg, b["idx"], dict(cnt=b["cnt"], ntok_rank=b["ntok"], off=b["off"], slot=b["slot"]), ws,
-                      with_recv_token=False)
+        ep.route_layout(cfg, b["logits"], dict(idx=b["idx"], w=b["wt"], cnt=b["cnt"], ntok_rank=b["ntok"],
+                                               off=b["off"], slot=b["slot"]), ws, with_recv_token=False)
         ep.get_rank_layout(cfg, b["idx"], dict(rank_count=b["rcnt"], rank_offset=b["roff"], rank_slot=b["rslot"]),
                            rws, with_rank_token=False)
         ep.dispatch(cfg, b["x"], b["rslot"], "fp8", b["recv"], b["scales"])
@@ -665,23 +660,21 @@ def run_dedup(args, w):
     def launch(i, rec):
         p = ptr[i]
         rec(0)
-        check(lib.ep_route(cp, p["logits"], p["idx"], p["wt"], sh), "ep_route")
+        check(lib.ep_route_layout(cp, p["logits"], p["idx"], p["wt"], p["cnt"], p["ntok"], p["off"], p["slot"], None,
+                                  ws.data_ptr(), ws.numel(), sh), "ep_route_layout")
         rec(1)
-        check(lib.ep_get_layout(cp, p["idx"], p["cnt"], p["ntok"], p["off"], p["slot"], None, ws.data_ptr(),
-                                ws.numel(), sh), "ep_get_layout")
-        rec(2)
         check(lib.ep_get_rank_layout(cp, p["idx"], p["rcnt"], p["roff"], p["rslot"], None, rws.data_ptr(),
                                      rws.numel(), sh), "ep_get_rank_layout")
-        rec(3)
+        rec(2)
         check(lib.ep_dispatch(cp, p["x"], p["rslot"], L.EP_RECV_FP8_E4M3, p["recv"], p["scales"], sh), "ep_dispatch")
-        rec(4)
+        rec(3)
         check(lib.ep_combine_rank_partial(cp, p["y"], p["idx"], p["slot"], p["wt"], p["rslot"], p["partial"], sh),
               "ep_combine_rank_partial")
-        rec(5)
+        rec(4)
         check(lib.ep_combine_ranks(cp, p["partial"], p["rslot"], p["out"], sh), "ep_combine_ranks")
-        rec(6)
+        rec(5)
 
-    stages = ("route", "layout", "rank_layout", "dispatch", "partial", "combine_ranks")
+    stages = ("route_layout", "rank_layout", "dispatch", "partial", "combine_ranks")
     dur, wall = timed_steps(args, nsets, launch, stages)
     kt = kernel_table(dur, bytes_)
     avg = {s: kt[s]["avg_us"] * 1e-6 for s in stages}

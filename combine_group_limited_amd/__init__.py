@@ -20,6 +20,8 @@ from .api import (  # noqa: F401
     layout_workspace_bytes,
     rank_layout_workspace_bytes,
     route,
+    route_layout,
+    route_layout_workspace_bytes,
     scores,
     validate,
 )

@@ -43,6 +43,8 @@ EXPORTS = (
     "ep_layout_workspace_bytes",
     "ep_get_layout",
     "ep_get_layout_static",
+    "ep_route_layout_workspace_bytes",
+    "ep_route_layout",
     "ep_dispatch",
     "ep_combine",
     "ep_dispatch_ll",
@@ -107,6 +109,10 @@ def lib() -> ctypes.CDLL:
         L.ep_get_layout.restype = I
         L.ep_get_layout_static.argtypes = [C, P, P, P, P, P, P, P]
         L.ep_get_layout_static.restype = I
+        L.ep_route_layout_workspace_bytes.argtypes = [C]
+        L.ep_route_layout_workspace_bytes.restype = ctypes.c_size_t
+        L.ep_route_layout.argtypes = [C, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
+        L.ep_route_layout.restype = I
         L.ep_dispatch.argtypes = [C, P, P, I, P, P, P]
         L.ep_dispatch.restype = I
         L.ep_combine.argtypes = [C, P, P, P, P, P]

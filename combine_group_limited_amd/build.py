@@ -50,8 +50,11 @@ def _inputs():
 
 
 def source_hash(inputs=None) -> str:
-    """SHA-256 over the compiler flags and the name and bytes of every input."""
-    h = hashlib.sha256("\0".join(HIPFLAGS).encode())
+    """SHA-256 over the compiler flags (include directories by name only, so
+    that a copy of the tree at another path matches) and the name and bytes
+    of every input."""
+    flags = [os.path.basename(f) if os.path.isabs(f) else f for f in HIPFLAGS]
+    h = hashlib.sha256("\0".join(flags).encode())
     for p in (inputs if inputs is not None else _inputs()):
         h.update(os.path.basename(p).encode() + b"\0")
         with open(p, "rb") as f:

@@ -1,4 +1,4 @@
-// gate.hip -- group-limited top-k gating, one 64-lane wavefront per token.
+// gate.hip -- group-limited top-k gating.
 //
 // Group-limited gating is named by the DeepEP pages (news report on the
 // release, feature list; German summary page "DeepEP"); the pages give no
@@ -7,19 +7,25 @@
 // index asc); the k best experts in those groups (score desc, index asc);
 // weights s_j / ((s_0 + s_1) + ... ).
 //
-// Lane l holds experts l, l + 64, l + 128, ... (EPL of them), so every
-// logits load instruction of a wave reads 256 contiguous bytes.
-//
-// Two kernels compute the same result:
-//  - gate_fast_kernel, when the group size GS = E/G divides 64 and m <= 2,
-//    or when every group is kept (TG = G): a group is then an aligned run of
-//    GS lanes inside one register, and its top-m is a butterfly merge of
-//    sorted pairs across those lanes (DPP lane swaps).  The k picks are k
-//    rounds of a 32-bit DPP wave maximum of the lanes' best candidate keys,
-//    with a ballot to find the owning lane (the lowest expert index among
-//    exact ties).  No LDS, no barriers.
+// Three kernels compute the same result:
+//  - gate_pair_kernel, two tokens per wavefront (one per 32-lane half, each
+//    lane holding a run of E/32 consecutive experts), when 32 divides E
+//    (128 <= E <= 1024), m <= 2 and a group is a power-of-two run of whole
+//    lanes (or TG = G).  Group scores are mostly in-lane, and each
+//    cross-lane step serves both tokens.  It can also count its picks per
+//    workgroup for the routing layout (HIST).
+//  - gate_fast_kernel, one wavefront per token, lane l holding experts l,
+//    l + 64, ..., when the group size GS = E/G divides 64 and m <= 2, or
+//    TG = G: a group is an aligned run of GS lanes inside one register, and
+//    its top-m is a butterfly merge of sorted pairs across those lanes (DPP
+//    lane swaps).  The k picks are k rounds of a 32-bit DPP wave maximum of
+//    the lanes' best candidate keys, with a ballot to find the owning lane
+//    (the lowest expert index among exact ties).  No LDS, no barriers.
 //  - gate_kernel, any shape: scores staged in LDS, lane g ranks group g's
 //    scores serially, k rounds of a 64-bit wave arg-max.
+//
+// Measured on MI355X at 4096 tokens, 256 experts in 8 groups, top-4 groups,
+// top-8 (HIP events): gate_fast_kernel 8.9 us, gate_pair_kernel 7.2 us.
 #include "device.h"
 #include "launch.h"
 
@@ -27,7 +33,7 @@ namespace ep {
 
 namespace {
 
-constexpr int kGateWaves = 4;  // tokens per workgroup
+constexpr int kGateWaves = 4;  // wavefronts per workgroup of the one-token-per-wavefront kernels
 constexpr int kMaxTopm = 8;
 
 // Keys of candidate experts: score bits with the top bit set (scores are
@@ -160,6 +166,182 @@ __global__ __launch_bounds__(kGateWaves * kWave) void gate_fast_kernel(
     }
 }
 
+// Two tokens per wavefront, one per 32-lane half: lane l of half h holds
+// the EPL = E / 32 consecutive experts [l*EPL, (l+1)*EPL) of token
+// 2 * (wavefront index) + h.  Used when 32 divides E and a group is a
+// power-of-two run of whole lanes (LPG = GS / EPL lanes, or every group
+// kept), with m <= 2.  A group's top-m is then mostly in-lane, and every
+// cross-lane step (group merge, pick maximum, ballot) serves both tokens
+// with one instruction, which halves the per-token instruction count of
+// the one-token-per-wavefront kernel.
+//
+// Picks: each round takes the largest candidate key of each half (DPP
+// maximum within the half, read from lanes 31 and 63); the owner is the
+// lowest lane holding it, and inside the owner the lowest of its experts
+// with that key, which is the lowest expert index among exact ties since
+// lanes hold ascending runs of experts.
+constexpr uint64_t kHiHalf = 0xFFFFFFFF00000000ull;
+constexpr int kPairWaves = 8;                // waves per workgroup
+constexpr int kPairTokens = 2 * kPairWaves;  // tokens per workgroup (one histogram column)
+constexpr int kMaxExpertsHist = 1024;
+
+//
+// With HIST, the workgroup (kPairTokens tokens, one "column") also counts
+// its picks for the routing layout: column c = blockIdx.x gets hist[c][e]
+// = picks of expert e and rank_hist[c][r] = tokens with at least one pick
+// on virtual rank r (its first pick there), as bytes (at most kPairTokens
+// each, since a token's picks are distinct experts).  The layout's assign
+// step sums these columns instead of a separate counting launch.
+template <int EPL, int MC, bool HIST>
+__global__ __launch_bounds__(kPairWaves * kWave) void gate_pair_kernel(
+    const float* __restrict__ logits, int32_t* __restrict__ topk_idx, float* __restrict__ topk_w, int T, int E,
+    int G, int TG, int k, int m, int lpg_log2, uint8_t* __restrict__ hist, uint8_t* __restrict__ rank_hist, int R,
+    int EPR) {
+    __shared__ int cnt_lds[HIST ? 2 * kMaxExpertsHist : 1];  // E expert counts, then R rank counts
+    // the wave index is uniform across the wavefront: read it into a scalar
+    // register so that the row resource below is uniform too
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    const int half = lane >> 5;
+    const int hl = lane & 31;
+    const int t0 = (blockIdx.x * kPairWaves + wave) * 2;
+    if (!HIST && t0 >= T) return;  // the whole wave leaves; nothing below synchronises
+    if (HIST)
+        for (int i = threadIdx.x; i < E + R; i += blockDim.x) cnt_lds[i] = 0;
+    const bool wlive = t0 < T;  // uniform: this wave has a token
+    const int t = t0 + half;
+    const bool live = t < T;  // the last wave's second half may have no token
+    int my_e = 0;
+    if (wlive) {
+
+    // 1. scores: EPL consecutive logits per lane, 16-byte loads through one
+    //    resource over the wave's rows (every address is a multiple of 4
+    //    bytes; a half with no token reads zeros and is masked below)
+    uint32_t sb[EPL];
+    {
+        const int ntok = T - t0 < 2 ? T - t0 : 2;
+        const auto rr = buffer_rsrc(logits + (size_t)t0 * E, (uint32_t)(ntok * E) * 4u);
+        const int base = (half * E + hl * EPL) * 4;
+#pragma unroll
+        for (int i = 0; i < EPL; i += 4) {
+            const i32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rr, base + i * 4, 0, kCached);
+            sb[i + 0] = __float_as_uint(sigmoid(__int_as_float(v.x)));
+            sb[i + 1] = __float_as_uint(sigmoid(__int_as_float(v.y)));
+            sb[i + 2] = __float_as_uint(sigmoid(__int_as_float(v.z)));
+            sb[i + 3] = __float_as_uint(sigmoid(__int_as_float(v.w)));
+        }
+    }
+
+    // 2. kept groups: the group of this lane is g = hl >> lpg_log2
+    bool kept = true;
+    if (MC > 0) {
+        // sorted best-MC list of the lane's scores (bit order = value order
+        // for these non-negative floats), then merged over the group's lanes
+        uint32_t a0 = sb[0], a1 = 0u;
+#pragma unroll
+        for (int i = 1; i < EPL; ++i) {
+            if (MC == 2) {
+                const uint32_t lo = min(a0, sb[i]);
+                a0 = max(a0, sb[i]);
+                a1 = max(a1, lo);
+            } else {
+                a0 = max(a0, sb[i]);
+            }
+        }
+        merge_step<1, MC>(a0, a1, lpg_log2);
+        merge_step<2, MC>(a0, a1, lpg_log2);
+        merge_step<4, MC>(a0, a1, lpg_log2);
+        merge_step<8, MC>(a0, a1, lpg_log2);
+        merge_step<16, MC>(a0, a1, lpg_log2);
+        float gf = __uint_as_float(a0);
+        if (MC == 2 && m == 2) gf = gf + __uint_as_float(a1);
+        const uint32_t mine = __float_as_uint(gf);
+        // rank of this lane's group among the G groups of its half
+        const int g = hl >> lpg_log2;
+        int rank = 0;
+        for (int o = 0; o < G; ++o) {
+            const uint32_t v = (uint32_t)__shfl((int)mine, (half << 5) + (o << lpg_log2), kWave);
+            rank += (v > mine || (v == mine && o < g)) ? 1 : 0;
+        }
+        kept = rank < TG;
+    }
+
+    // 3. candidate keys (non-candidates, and a half with no token, hold 0)
+    uint32_t key[EPL];
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) key[i] = (kept && live) ? (sb[i] | kCandidate) : 0u;
+
+    // 4. k rounds
+    uint32_t my_s = 0u;
+    float S = 0.0f;
+    const uint32_t hsel = half ? ~0u : 0u;  // selects the upper half's value of a pair
+    for (int j = 0; j < k; ++j) {
+        uint32_t bk = key[0];
+#pragma unroll
+        for (int i = 1; i < EPL; ++i) bk = max(bk, key[i]);
+        // maximum of each half: row butterflies, then rows 0 -> 1 and 2 -> 3
+        uint32_t v = bk;
+        v = max(v, dpp_u32<kDppXor1>(v));
+        v = max(v, dpp_u32<kDppXor2>(v));
+        v = max(v, dpp_u32<kDppHalfMirror>(v));
+        v = max(v, dpp_u32<kDppMirror>(v));
+        v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, kDppRowBcast15, 0xA, 0xF, false));
+        const uint32_t m0 = (uint32_t)__builtin_amdgcn_readlane((int)v, 31);
+        const uint32_t m1 = (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+        const uint32_t tgt = m0 ^ ((m0 ^ m1) & hsel);
+        const uint64_t eq = __ballot(bk == tgt);
+        const int o0 = __ffsll((unsigned long long)(eq & ~kHiHalf)) - 1;
+        const int o1 = __ffsll((unsigned long long)(eq & kHiHalf)) - 1;
+        // the owner lanes take their first key equal to the maximum; `open`
+        // and `hit` stay per-lane booleans (lane masks), so the clears are
+        // selects on those masks
+        bool open = lane == o0 || lane == o1;
+        uint32_t ii = 0u;
+#pragma unroll
+        for (int i = 0; i < EPL; ++i) {
+            const bool hit = open && key[i] == bk;
+            open = open && !hit;
+            key[i] = hit ? 0u : key[i];
+            ii = hit ? (uint32_t)i : ii;
+        }
+        const uint32_t e0 = (uint32_t)(o0 * EPL) + (uint32_t)__builtin_amdgcn_readlane((int)ii, o0);
+        const uint32_t e1 = (uint32_t)((o1 - 32) * EPL) + (uint32_t)__builtin_amdgcn_readlane((int)ii, o1);
+        const int e = (int)(e0 ^ ((e0 ^ e1) & hsel));
+        my_e = hl == j ? e : my_e;
+        my_s = hl == j ? tgt : my_s;
+        S = S + __uint_as_float(tgt & ~kCandidate);
+    }
+
+    // 5. weights
+    if (live && hl < k) {
+        topk_idx[(size_t)t * k + hl] = my_e;
+        topk_w[(size_t)t * k + hl] = __uint_as_float(my_s & ~kCandidate) / S;
+    }
+    }  // wlive
+
+    if (HIST) {
+        // a pick is the token's first on its rank when no earlier pick of
+        // the token (lanes hl' < hl of the half) has the same rank; the
+        // shuffles run with every lane active
+        const bool pick = wlive && live && hl < k;
+        const int r = pick ? my_e / EPR : -1;
+        bool first = pick;
+        for (int jj = 0; jj + 1 < k; ++jj) {
+            const int rj = __shfl(r, (half << 5) + jj, kWave);
+            first = first && !(jj < hl && rj == r);
+        }
+        __syncthreads();  // counters cleared
+        if (pick) {
+            atomicAdd(&cnt_lds[my_e], 1);
+            if (first) atomicAdd(&cnt_lds[E + r], 1);
+        }
+        __syncthreads();
+        const size_t c = blockIdx.x;
+        for (int i = threadIdx.x; i < E; i += blockDim.x) hist[c * E + i] = (uint8_t)cnt_lds[i];
+        for (int i = threadIdx.x; i < R; i += blockDim.x) rank_hist[c * R + i] = (uint8_t)cnt_lds[E + i];
+    }
+}
+
 template <int EPL>
 __global__ __launch_bounds__(kGateWaves * kWave) void gate_kernel(
     const float* __restrict__ logits, int32_t* __restrict__ topk_idx, float* __restrict__ topk_w,
@@ -287,6 +469,50 @@ hipError_t launch_fast(const Shape& s, int gs_log2, const float* logits, int32_t
     return hipGetLastError();
 }
 
+template <int EPL, int MC>
+hipError_t launch_pair(const Shape& s, int lpg_log2, const float* logits, int32_t* idx, float* w, uint8_t* hist,
+                       uint8_t* rank_hist, hipStream_t st) {
+    const int blocks = (s.T + kPairTokens - 1) / kPairTokens;
+    if (hist)
+        hipLaunchKernelGGL((gate_pair_kernel<EPL, MC, true>), dim3(blocks), dim3(kPairWaves * kWave), 0, st, logits,
+                           idx, w, s.T, s.E, s.G, s.TG, s.k, s.m, lpg_log2, hist, rank_hist, s.R, s.E / s.R);
+    else
+        hipLaunchKernelGGL((gate_pair_kernel<EPL, MC, false>), dim3(blocks), dim3(kPairWaves * kWave), 0, st, logits,
+                           idx, w, s.T, s.E, s.G, s.TG, s.k, s.m, lpg_log2, nullptr, nullptr, s.R, s.E / s.R);
+    return hipGetLastError();
+}
+
+template <int EPL>
+hipError_t launch_pair_mc(const Shape& s, int mc, int lpg_log2, const float* logits, int32_t* idx, float* w,
+                          uint8_t* hist, uint8_t* rank_hist, hipStream_t st) {
+    if (mc == 0) return launch_pair<EPL, 0>(s, lpg_log2, logits, idx, w, hist, rank_hist, st);
+    if (mc == 1) return launch_pair<EPL, 1>(s, lpg_log2, logits, idx, w, hist, rank_hist, st);
+    return launch_pair<EPL, 2>(s, lpg_log2, logits, idx, w, hist, rank_hist, st);
+}
+
+// The two-tokens-per-wavefront kernel applies: 32 | E with 4 <= E/32 <= 32
+// (E/32 experts per lane, read 16 bytes at a time), m <= 2, and either every
+// group is kept or a group is a power-of-two run of whole lanes of a half.
+bool pair_gate_shape(const Shape& s, int* epl, int* lpg_log2, int* mc) {
+    if (s.E % 32 != 0 || s.E < 128 || s.E > 1024 || s.m > 2) return false;
+    const int GS = s.E / s.G;
+    *epl = s.E / 32;
+    *lpg_log2 = 0;
+    while ((*epl << *lpg_log2) < GS) ++*lpg_log2;
+    const bool lanes_ok = GS % *epl == 0 && (*epl << *lpg_log2) == GS && (1 << *lpg_log2) <= 32;
+    if (s.TG != s.G && !lanes_ok) return false;
+    *mc = s.TG == s.G ? 0 : s.m;
+    return true;
+}
+
+hipError_t launch_pair_any(const Shape& s, int epl, int lpg_log2, int mc, const float* logits, int32_t* idx,
+                           float* w, uint8_t* hist, uint8_t* rank_hist, hipStream_t st) {
+    if (epl == 4) return launch_pair_mc<4>(s, mc, lpg_log2, logits, idx, w, hist, rank_hist, st);
+    if (epl == 8) return launch_pair_mc<8>(s, mc, lpg_log2, logits, idx, w, hist, rank_hist, st);
+    if (epl == 16) return launch_pair_mc<16>(s, mc, lpg_log2, logits, idx, w, hist, rank_hist, st);
+    return launch_pair_mc<32>(s, mc, lpg_log2, logits, idx, w, hist, rank_hist, st);
+}
+
 template <int EPL>
 hipError_t launch_fast_mc(const Shape& s, int mc, int gs_log2, const float* logits, int32_t* idx, float* w,
                           hipStream_t st) {
@@ -324,6 +550,11 @@ __global__ __launch_bounds__(256) void scores_kernel(const float* logits, float*
 hipError_t launch_route(const Shape& s, const float* logits, int32_t* topk_idx, float* topk_w,
                         hipStream_t stream) {
     if (s.T == 0) return hipSuccess;
+    {
+        int pepl = 0, lpg_log2 = 0, pmc = 0;
+        if (pair_gate_shape(s, &pepl, &lpg_log2, &pmc))
+            return launch_pair_any(s, pepl, lpg_log2, pmc, logits, topk_idx, topk_w, nullptr, nullptr, stream);
+    }
     const int epl = (s.E + kWave - 1) / kWave;
     const int GS = s.E / s.G;
     int gs_log2 = 0;
@@ -343,6 +574,23 @@ hipError_t launch_route(const Shape& s, const float* logits, int32_t* topk_idx, 
     if (epl <= 4) return launch_gate<4>(s, logits, topk_idx, topk_w, stream);
     if (epl <= 8) return launch_gate<8>(s, logits, topk_idx, topk_w, stream);
     return launch_gate<16>(s, logits, topk_idx, topk_w, stream);
+}
+
+bool route_hist_supported(const Shape& s) {
+    int epl, lpg_log2, mc;
+    return s.E <= kMaxExpertsHist && s.R <= s.E && pair_gate_shape(s, &epl, &lpg_log2, &mc);
+}
+
+int route_hist_columns(const Shape& s) { return (s.T + kPairTokens - 1) / kPairTokens; }
+
+int route_hist_column_tokens() { return kPairTokens; }
+
+hipError_t launch_route_hist(const Shape& s, const float* logits, int32_t* topk_idx, float* topk_w, uint8_t* hist,
+                             uint8_t* rank_hist, hipStream_t stream) {
+    if (s.T == 0) return hipSuccess;
+    int epl = 0, lpg_log2 = 0, mc = 0;
+    if (!pair_gate_shape(s, &epl, &lpg_log2, &mc)) return hipErrorInvalidValue;
+    return launch_pair_any(s, epl, lpg_log2, mc, logits, topk_idx, topk_w, hist, rank_hist, stream);
 }
 
 hipError_t launch_scores(const Shape& s, const float* logits, float* scores, hipStream_t stream) {

@@ -19,10 +19,25 @@ hipError_t launch_route(const Shape& s, const float* logits, int32_t* topk_idx, 
                         hipStream_t stream);
 hipError_t launch_scores(const Shape& s, const float* logits, float* scores, hipStream_t stream);
 
+// Routing that also counts its picks per column of route_hist_column_tokens()
+// tokens: hist [columns][E] and rank_hist [columns][R] bytes (gate.hip);
+// the layout's assign step then reads these columns (layout.hip).
+bool route_hist_supported(const Shape& s);
+int route_hist_columns(const Shape& s);
+int route_hist_column_tokens();
+hipError_t launch_route_hist(const Shape& s, const float* logits, int32_t* topk_idx, float* topk_w, uint8_t* hist,
+                             uint8_t* rank_hist, hipStream_t stream);
+
 size_t layout_workspace_bytes(const Shape& s);
 hipError_t launch_layout(const Shape& s, const int32_t* topk_idx, int32_t* cnt, int32_t* ntok_rank,
                          int32_t* off, int32_t* slot, int32_t* recv_token, void* ws,
                          hipStream_t stream);
+
+// The layout from route_hist's columns in one launch (layout.hip).
+bool layout_from_hist_supported(const Shape& s);
+hipError_t launch_layout_from_hist(const Shape& s, const int32_t* topk_idx, const uint8_t* hist,
+                                   const uint8_t* rank_hist, int C, int CT, int32_t* cnt, int32_t* ntok_rank,
+                                   int32_t* off, int32_t* slot, int32_t* recv_token, hipStream_t stream);
 
 // Per-rank deduplicated layout (the layout over "first pick of the token on
 // this rank" entries, one bucket per rank).

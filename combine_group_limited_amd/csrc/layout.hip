@@ -150,23 +150,20 @@ __global__ __launch_bounds__(kScanThreads) void layout_scan_kernel(int32_t* __re
     }
 }
 
-// Ranks inside one block of NT = W*64 consecutive pairs: each wavefront
-// sets one bit per pair in an LDS mask per expert (64-bit atomic OR, which
-// commutes), and a pair's rank within its wavefront is the popcount of the
-// mask bits of the lanes before it.  `base[e]` holds the row of the block's
-// first pair with expert e.  Writes slot and recv_token for the block.
+// Ranks inside one block of NT = W*64 consecutive pairs starting at pair
+// p0 (thread tid takes pair p0 + tid, whose expert id `e` the caller has
+// read: -1 if unrouted or past the end): each wavefront sets one bit per pair
+// in an LDS mask per expert (64-bit atomic OR, which commutes), and a pair's
+// rank within its wavefront is the popcount of the mask bits of the lanes
+// before it.  `base[e]` holds the row of the block's first pair with expert
+// e.  Writes slot and recv_token for the pairs below P.
 template <int W>
-__device__ void assign_block(const int32_t* __restrict__ idx, const int32_t* base, uint64_t* mask, int32_t* wpre,
+__device__ void assign_pairs(int e, long p0, const int32_t* base, uint64_t* mask, int32_t* wpre,
                              int32_t* __restrict__ slot, int32_t* __restrict__ recv_token, long P, int k, int E,
-                             int total, int c) {
+                             int total) {
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     constexpr int NT = W * 64;
-    const long p = (long)c * NT + tid;
-    int e = -1;
-    if (p < P) {
-        const int v = idx[p];
-        if ((unsigned)v < (unsigned)E) e = v;
-    }
+    const long p = p0 + tid;
     __syncthreads();
     if (e >= 0) atomicOr(reinterpret_cast<unsigned long long*>(&mask[wave * E + e]), 1ull << lane);
     __syncthreads();
@@ -183,11 +180,28 @@ __device__ void assign_block(const int32_t* __restrict__ idx, const int32_t* bas
         if (e >= 0) {
             const uint64_t before = mask[wave * E + e] & ((1ull << lane) - 1ull);
             s = base[e] + wpre[wave * E + e] + __popcll(before);
-            if (recv_token) recv_token[s] = (int32_t)(p / k);
+            // rows lie below `total` by construction; the bound keeps a store
+            // inside recv_token even if the counts were inconsistent
+            if (recv_token && (unsigned)s < (unsigned)total) recv_token[s] = (int32_t)(p / k);
         }
         slot[p] = s;
         if (recv_token && p >= total) recv_token[p] = -1;
     }
+}
+
+// expert id of pair p for the assign step: -1 if unrouted or p >= P
+__device__ __forceinline__ int pair_expert(const int32_t* __restrict__ idx, long p, long P, int E) {
+    if (p >= P) return -1;
+    const int v = idx[p];
+    return (unsigned)v < (unsigned)E ? v : -1;
+}
+
+template <int W>
+__device__ void assign_block(const int32_t* __restrict__ idx, const int32_t* base, uint64_t* mask, int32_t* wpre,
+                             int32_t* __restrict__ slot, int32_t* __restrict__ recv_token, long P, int k, int E,
+                             int total, int c) {
+    const long p0 = (long)c * (W * 64);
+    assign_pairs<W>(pair_expert(idx, p0 + threadIdx.x, P, E), p0, base, mask, wpre, slot, recv_token, P, k, E, total);
 }
 
 template <int W>
@@ -382,6 +396,152 @@ __global__ __launch_bounds__(W * 64) void layout_small_kernel(
     }
 }
 
+// column loads in flight per thread (added as packed bytes 15 at a time:
+// 15 * 16 < 256 keeps the byte sums exact)
+constexpr int kColBatch = 32;
+
+// Layout from the routing step's per-column histograms (route_hist:
+// columns of CT tokens, hist [C][E] and rank_hist [C][R] bytes), in one
+// launch.  Block b takes the CB columns [b*CB, (b+1)*CB), i.e. the pairs of
+// tokens [b*CB*CT, (b+1)*CB*CT), in chunks of NT = W*64 pairs:
+//  1. per expert, the sum of all columns (its count) and of the columns
+//     before the block (its rows before the block).  A 4-byte load holds
+//     four experts' counts of one column; kColBatch loads are issued
+//     together and added as packed bytes, unpacked after every fifteen (a
+//     column count is at most CT = 16, so fifteen of them fit a byte).  Thread (g, d) sums
+//     dword d of the rows g, g + NG, ... (NG = NT / (E/4) row groups), then
+//     the groups meet in LDS.
+//  2. expert offsets by a block-wide scan; block 0 writes the counts,
+//     offsets and per-rank token counts.
+//  3. slots as in assign_pairs, chunk by chunk, carrying each expert's next
+//     row; the first chunk's expert ids are read at the start, so that load
+//     overlaps step 1.
+template <int W>
+__global__ __launch_bounds__(W * 64) void layout_assign_cols_kernel(
+    const int32_t* __restrict__ idx, const uint8_t* __restrict__ hist, const uint8_t* __restrict__ rank_hist,
+    int32_t* __restrict__ cnt, int32_t* __restrict__ ntok_rank, int32_t* __restrict__ off,
+    int32_t* __restrict__ slot, int32_t* __restrict__ recv_token, long P, int k, int E, int R, int C, int CB,
+    int CT) {
+    extern __shared__ __align__(16) unsigned char ac_sm[];
+    constexpr int NT = W * 64;
+    const int ED = E >> 2;   // dwords per histogram row
+    const int NG = NT / ED;  // row groups
+    uint64_t* mask = reinterpret_cast<uint64_t*>(ac_sm);        // [W][E]
+    int32_t* wpre = reinterpret_cast<int32_t*>(mask + W * E);    // [W][E]; expert totals before step 3
+    int32_t* base = wpre + W * E;                                // [E]
+    int32_t* red = base + E;                                     // [2][NG][E]: sums before the block, all
+    int32_t* rtot = red + 2 * NG * E;                            // [R]
+    __shared__ int wsum[W];
+    const int tid = threadIdx.x;
+    const int c0 = blockIdx.x * CB;
+    const long p_begin = (long)c0 * CT * k;
+    const long p_end = min(P, (long)(c0 + CB) * CT * k);
+    int e_first = pair_expert(idx, p_begin + tid, p_end, E);
+
+    for (int i = tid; i < W * E; i += NT) mask[i] = 0ull;
+    for (int i = tid; i < R; i += NT) rtot[i] = 0;
+    {
+        // NG = NT / ED exactly, so every thread has a g < NG.  Loads go out
+        // kColBatch at a time (independent registers) and are added as
+        // packed bytes, 15 at a time (15 counts of at most CT = 16 fit a byte).
+        const int d = tid % ED, g = tid / ED;
+        const uint32_t* h32 = reinterpret_cast<const uint32_t*>(hist) + d;
+        int pre[4] = {0, 0, 0, 0}, all[4] = {0, 0, 0, 0};
+        for (int r0 = g; r0 < C; r0 += kColBatch * NG) {
+            uint32_t v[kColBatch];
+#pragma unroll
+            for (int u = 0; u < kColBatch; ++u) {
+                const int r = r0 + u * NG;
+                v[u] = r < C ? h32[(size_t)r * ED] : 0u;
+            }
+            uint32_t pp = 0u, pa = 0u;
+#pragma unroll
+            for (int u = 0; u < kColBatch; ++u) {
+                pa += v[u];
+                pp += (r0 + u * NG < c0) ? v[u] : 0u;
+                if (u % 15 == 14 || u == kColBatch - 1) {  // at most 15 packed counts per byte
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        pre[q] += (int)((pp >> (8 * q)) & 0xFFu);
+                        all[q] += (int)((pa >> (8 * q)) & 0xFFu);
+                    }
+                    pp = pa = 0u;
+                }
+            }
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            red[g * E + 4 * d + q] = pre[q];
+            red[(NG + g) * E + 4 * d + q] = all[q];
+        }
+    }
+    if (blockIdx.x == 0) {
+        // tokens per rank: thread (g, r) sums byte r of the rows g, g + NR,
+        // ... (R divides NT, so every thread has a g < NR)
+        const int NR = NT / R;
+        const int rr = tid % R, g = tid / R;
+        int acc = 0;
+        for (int r0 = g; r0 < C; r0 += kColBatch * NR) {
+            uint32_t v[kColBatch];  // issued together, like the expert columns
+#pragma unroll
+            for (int u = 0; u < kColBatch; ++u) {
+                const int row = r0 + u * NR;
+                v[u] = row < C ? rank_hist[(size_t)row * R + rr] : 0u;
+            }
+#pragma unroll
+            for (int u = 0; u < kColBatch; ++u) acc += (int)v[u];
+        }
+        __syncthreads();  // rtot cleared
+        atomicAdd(&rtot[rr], acc);
+    }
+    __syncthreads();
+    for (int e = tid; e < E; e += NT) {
+        int before = 0, all = 0;
+        for (int g = 0; g < NG; ++g) {
+            before += red[g * E + e];
+            all += red[(NG + g) * E + e];
+        }
+        base[e] = before;
+        wpre[e] = all;
+    }
+    __syncthreads();
+    if (blockIdx.x == 0)
+        for (int i = tid; i < R; i += NT) ntok_rank[i] = rtot[i];
+
+    // expert offsets: each thread scans EPT consecutive experts
+    const int EPT = (E + NT - 1) / NT;
+    const int e0 = tid * EPT;
+    int local = 0;
+    for (int i = 0; i < EPT; ++i)
+        if (e0 + i < E) local += wpre[e0 + i];
+    int total;
+    int ex = block_exclusive_sum(local, &total, wsum);
+    for (int i = 0; i < EPT; ++i) {
+        const int e = e0 + i;
+        if (e < E) {
+            const int t_e = wpre[e];
+            base[e] += ex;
+            if (blockIdx.x == 0) {
+                off[e] = ex;
+                cnt[e] = t_e;
+            }
+            ex += t_e;
+        }
+    }
+    if (blockIdx.x == 0 && tid == 0) off[E] = total;
+
+    for (long p0 = p_begin; p0 < p_end; p0 += NT) {
+        const int e = p0 == p_begin ? e_first : pair_expert(idx, p0 + tid, p_end, E);
+        assign_pairs<W>(e, p0, base, mask, wpre, slot, recv_token, p_end, k, E, total);
+        __syncthreads();
+        // the next chunk's rows start after this chunk's pairs
+        for (int i = tid; i < E; i += NT) {
+            base[i] += wpre[(W - 1) * E + i] + __popcll(mask[(W - 1) * E + i]);
+            for (int w = 0; w < W; ++w) mask[w * E + i] = 0ull;
+        }
+    }
+}
+
 template <int W>
 hipError_t launch_assign(const Shape& s, long P, int C, const int32_t* idx, const int32_t* hist,
                          const int32_t* cnt, int32_t* off, int32_t* slot, int32_t* recv_token,
@@ -475,6 +635,45 @@ hipError_t launch_layout(const Shape& s, const int32_t* topk_idx, int32_t* cnt, 
     if (e != hipSuccess) return e;
     if (W == 8) return launch_assign<8>(s, P, C, topk_idx, hist, cnt, off, slot, recv_token, stream);
     return launch_assign<4>(s, P, C, topk_idx, hist, cnt, off, slot, recv_token, stream);
+}
+
+// Columns of the routing step's histograms per assign block (CB) and the
+// launch shape of layout_assign_cols_kernel; false if the shape does not
+// fit its limits (E/4 dwords per histogram row must divide the block, the
+// ranks must fit the block, and the LDS must fit 64 KiB).
+namespace {
+constexpr int kColsPerAssignBlock = 4;
+constexpr size_t kColsMaxLds = 65536;
+
+size_t cols_lds_bytes(int W, int E, int R) {
+    const int NT = W * 64, NG = NT / (E / 4);
+    return (size_t)(12 * W + 4) * E + (size_t)2 * NG * E * 4 + (size_t)R * 4;
+}
+}  // namespace
+
+bool layout_from_hist_supported(const Shape& s) {
+    const int W = layout_waves(s.E);
+    const int NT = W * 64;
+    if (s.E % 4 != 0 || s.E / 4 > NT || NT % (s.E / 4) != 0) return false;
+    if (s.R > NT || NT % s.R != 0) return false;
+    return cols_lds_bytes(W, s.E, s.R) <= kColsMaxLds;
+}
+
+hipError_t launch_layout_from_hist(const Shape& s, const int32_t* topk_idx, const uint8_t* hist,
+                                   const uint8_t* rank_hist, int C, int CT, int32_t* cnt, int32_t* ntok_rank,
+                                   int32_t* off, int32_t* slot, int32_t* recv_token, hipStream_t stream) {
+    const long P = (long)s.T * s.k;
+    const int W = layout_waves(s.E);
+    const int CB = kColsPerAssignBlock;
+    const int blocks = C > 0 ? (C + CB - 1) / CB : 1;  // block 0 writes the counts even with no tokens
+    const size_t lds = cols_lds_bytes(W, s.E, s.R);
+    if (W == 8)
+        hipLaunchKernelGGL(layout_assign_cols_kernel<8>, dim3(blocks), dim3(8 * 64), lds, stream, topk_idx, hist,
+                           rank_hist, cnt, ntok_rank, off, slot, recv_token, P, s.k, s.E, s.R, C, CB, CT);
+    else
+        hipLaunchKernelGGL(layout_assign_cols_kernel<4>, dim3(blocks), dim3(4 * 64), lds, stream, topk_idx, hist,
+                           rank_hist, cnt, ntok_rank, off, slot, recv_token, P, s.k, s.E, s.R, C, CB, CT);
+    return hipGetLastError();
 }
 
 // Workspace: the rank-input array [T*k], R scratch counters, then the

@@ -57,7 +57,7 @@ extern "C" {
 
 #define EP_API __attribute__((visibility("default")))
 
-#define EP_ABI_VERSION 3
+#define EP_ABI_VERSION 4
 
 /* Return codes */
 #define EP_OK               0
@@ -166,6 +166,29 @@ EP_API int ep_get_layout(const ep_config_t* cfg, const int32_t* topk_idx,
                          int32_t* expert_offset, int32_t* slot,
                          int32_t* recv_token, void* workspace,
                          size_t workspace_bytes, void* stream);
+
+/* Bytes of device workspace ep_route_layout needs for `cfg` (0 if invalid). */
+EP_API size_t ep_route_layout_workspace_bytes(const ep_config_t* cfg);
+
+/* ep_route followed by ep_get_layout on its output, in fewer launches
+ * (the [DE] gating, then [DAY2] "DeepEP是什么" receive counts).  Arguments
+ * and results are those of the two calls (logits, topk_idx and topk_w as
+ * for ep_route; counts, offsets, slot and recv_token as for ep_get_layout),
+ * and the results are identical.  When 32 divides E (128 <= E <= 1024),
+ * m <= 2, a group covers whole 32-lane slices (or TG = G) and
+ * 1024 < T*k with T <= 4096, the routing kernel also counts its picks per
+ * block of 16 tokens into the workspace, and one more launch sums those
+ * counts, scans the offsets and assigns the rows, which saves the layout's
+ * counting launch; other shapes run the two calls' kernels.
+ *   workspace  device, >= ep_route_layout_workspace_bytes(cfg) bytes,
+ *              16-byte aligned; scratch after the call
+ * Errors as for ep_route and ep_get_layout. */
+EP_API int ep_route_layout(const ep_config_t* cfg, const float* logits,
+                           int32_t* topk_idx, float* topk_w,
+                           int32_t* cnt_expert, int32_t* ntok_rank,
+                           int32_t* expert_offset, int32_t* slot,
+                           int32_t* recv_token, void* workspace,
+                           size_t workspace_bytes, void* stream);
 
 /* Bytes of the device array ep_get_layout_static uses as its scratch. */
 #define EP_STATIC_SCRATCH_BYTES (1u << 20)

@@ -29,7 +29,7 @@ def test_every_declared_function_is_exported():
 
 def test_version_and_messages():
     lib = ep.lib()
-    assert lib.ep_abi_version() == 3
+    assert lib.ep_abi_version() == 4
     for code in (0, -1, -2, -3, -4, -5, -6, 42):
         assert len(lib.ep_strerror(code)) > 0
     assert lib.ep_last_hip_error() == 0
@@ -125,6 +125,30 @@ def test_layout_rejections():
                              None) == L.EP_ERR_INVALID_ARG
     assert lib.ep_get_layout(ctypes.byref(c), FAKE, FAKE, FAKE, FAKE, FAKE + 1, FAKE, FAKE, need,
                              None) == L.EP_ERR_ALIGNMENT
+
+
+def test_route_layout_rejections():
+    lib = ep.lib()
+    c = _cfg().c()
+    need = lib.ep_route_layout_workspace_bytes(ctypes.byref(c))
+    assert need > 0
+    # the two-launch path's workspace at prefill: a byte per expert and per
+    # rank for each 16-token column
+    assert need == 256 * 256 + 256 * 32
+    args = [FAKE] * 8
+    assert lib.ep_route_layout(ctypes.byref(c), *args, FAKE, need - 1, None) == L.EP_ERR_WORKSPACE
+    assert lib.ep_route_layout(ctypes.byref(c), *args, None, need, None) == L.EP_ERR_WORKSPACE
+    assert lib.ep_route_layout(ctypes.byref(c), *args, FAKE + 8, need, None) == L.EP_ERR_ALIGNMENT
+    assert lib.ep_route_layout(ctypes.byref(c), FAKE + 2, *args[1:], FAKE, need, None) == L.EP_ERR_ALIGNMENT
+    assert lib.ep_route_layout(ctypes.byref(c), None, *args[1:], FAKE, need, None) == L.EP_ERR_INVALID_ARG
+    assert lib.ep_route_layout(ctypes.byref(c), FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, need,
+                               None) == L.EP_ERR_INVALID_ARG
+    bad = _cfg(E=100).c()
+    assert lib.ep_route_layout_workspace_bytes(ctypes.byref(bad)) == 0
+    assert lib.ep_route_layout(ctypes.byref(bad), *args, FAKE, need, None) == L.EP_ERR_INVALID_ARG
+    # other shapes need the layout's own workspace
+    small = _cfg(T=64).c()
+    assert lib.ep_route_layout_workspace_bytes(ctypes.byref(small)) == lib.ep_layout_workspace_bytes(ctypes.byref(small))
 
 
 def test_layout_static_rejections():

@@ -102,3 +102,28 @@ def test_low_latency_and_dedup_steps_in_graph():
     # comparison (the eager writes between replays would change them)
     outs = [idx, wt, ll["count"], ll["slot"], out_ll, *lay.values(), *rl.values(), out_rk]
     _capture_and_check(run, outs)
+
+
+def test_fused_route_layout_step_in_graph():
+    # the step as the benchmark runs it: ep_route_layout (two launches at
+    # this size), FP8 dispatch, combine
+    w = W.PREFILL.replace(T=2048)
+    cfg = ep.Config.of(w)
+    lg = to_dev(W.gen_logits(w))
+    x = to_dev(W.gen_x(w), torch.bfloat16)
+    y = to_dev(W.gen_y(w), torch.bfloat16)
+    i32 = dict(dtype=torch.int32, device="cuda")
+    o = dict(idx=torch.empty((w.T, w.k), **i32), w=torch.empty((w.T, w.k), dtype=torch.float32, device="cuda"),
+             cnt=torch.empty(w.E, **i32), ntok_rank=torch.empty(w.R, **i32), off=torch.empty(w.E + 1, **i32),
+             slot=torch.empty((w.T, w.k), **i32), recv_token=torch.empty(w.nrows, **i32))
+    ws = torch.empty(ep.route_layout_workspace_bytes(cfg), dtype=torch.uint8, device="cuda")
+    recv = torch.empty((w.nrows, w.H), dtype=torch.uint8, device="cuda")
+    sc = torch.empty((w.nrows, w.H // 128), dtype=torch.float32, device="cuda")
+    out = torch.empty((w.T, w.H), dtype=torch.bfloat16, device="cuda")
+
+    def run():
+        ep.route_layout(cfg, lg, o, ws)
+        ep.dispatch(cfg, x, o["slot"], "fp8", recv, sc)
+        ep.combine(cfg, y, o["slot"], o["w"], out)
+
+    _capture_and_check(run, [*o.values(), recv, sc, out])

@@ -1,0 +1,136 @@
+"""ep_route_layout (routing followed by the layout, in two launches where
+the routing kernel also counts its picks per 16-token column) against the
+oracle's route and layout, bit for bit, and against the separate ep_route
+and ep_get_layout calls.  Shapes: every workload; random shapes of the
+two-tokens-per-wavefront gate (E in {128, 256, 512, 1024}, groups of whole
+32-lane slices or every group kept, m <= 2, k up to 32, any R) at token
+counts around the 16-token columns and the 64-token assign blocks, with
+normal and tie-heavy logits; and shapes that take the fallback path."""
+import numpy as np
+import pytest
+import torch
+
+import combine_group_limited_amd as ep
+import oracle
+import workloads as W
+from pipeline import to_dev, to_host
+
+pytestmark = pytest.mark.gpu
+
+KEYS = ("cnt", "off", "ntok_rank", "slot", "recv_token")
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+def check(w, lg, with_recv_token=True):
+    cfg = ep.Config.of(w)
+    d = to_dev(lg)
+    got = ep.route_layout(cfg, d, with_recv_token=with_recv_token)
+    idx, wt = ep.route(cfg, d)
+    lay = ep.get_layout(cfg, idx)
+    torch.cuda.synchronize()
+    oi, ow = oracle.route(lg, w.G, w.TG, w.k, w.topm)
+    ol = oracle.layout(oi, w.E, w.R)
+    assert np.array_equal(to_host(got["idx"]), oi), "idx"
+    assert np.array_equal(to_host(got["w"]).view(np.uint32), ow.view(np.uint32)), "w"
+    assert np.array_equal(to_host(idx), oi), "ep_route idx"
+    assert np.array_equal(to_host(wt).view(np.uint32), ow.view(np.uint32)), "ep_route w"
+    for key in KEYS:
+        if key == "recv_token" and not with_recv_token:
+            continue
+        assert np.array_equal(to_host(got[key]), ol[key]), key
+        assert np.array_equal(to_host(lay[key]), ol[key]), "ep_get_layout " + key
+
+
+@pytest.mark.parametrize("name", ["tiny", "decode", "prefill", "skewed", "skewed_literal", "large"])
+def test_route_layout_workloads(name):
+    w = W.CONFIGS[name]
+    say("route_layout", name, w)
+    check(w, W.gen_logits(w))
+
+
+def test_two_launch_path_is_taken_at_prefill():
+    # the workspace is the routing step's column histograms: one byte per
+    # expert and per rank for each of the 256 columns of 16 tokens
+    cfg = ep.Config.of(W.PREFILL)
+    C = W.PREFILL.T // 16
+    want = -(-C * cfg.E // 256) * 256 + -(-C * cfg.R // 256) * 256
+    assert ep.route_layout_workspace_bytes(cfg) == want
+
+
+def _pair_shape(rng):
+    E = int(rng.choice([128, 256, 512, 1024]))
+    if rng.random() < 0.25:
+        # every group kept: any G dividing E
+        G = int(rng.choice([g for g in (1, 2, 3, 4, 8, 16, 32, 64) if E % g == 0]))
+        TG, m = G, int(rng.choice([0, 1, 2]))
+    else:
+        G = int(rng.choice([1, 2, 4, 8, 16, 32]))  # groups of 32/G whole lanes
+        TG, m = int(rng.integers(1, G + 1)), int(rng.choice([0, 1, 2]))
+    GS = E // G
+    k = int(rng.integers(1, min(32, TG * GS) + 1))
+    if m == 0 and max(1, k // TG) > 2:
+        m = 2
+    m = min(m, GS)
+    R = int(rng.choice([r for r in (1, 2, 4, 8, 16, 32, 64, 128, 256, 512) if E % r == 0]))
+    if rng.random() < 0.7:   # above 1024 pairs: the two-launch path where the shape allows it
+        T = int(rng.choice([129, 255, 257, 1000, 1023, 2049, 4095, 4096]))
+    else:
+        T = int(rng.choice([1, 15, 16, 17, 63, 64, 65, 127]))
+    return W.Workload("pair", T=T, H=128, E=E, G=G, TG=TG, k=k, R=R, m=m, seed=int(rng.integers(1 << 30)))
+
+
+@pytest.mark.parametrize("case", range(32))
+def test_route_layout_random_pair_shapes(case):
+    rng = np.random.default_rng(7000 + case)
+    w = _pair_shape(rng)
+    mode = ("normal", "exact", "ulps")[case % 3]
+    say("route_layout random", case, mode, w)
+    if mode == "normal":
+        lg = W.gen_logits(w)
+    else:
+        vals = np.float32([-3.0, -0.5, 0.0, 0.75, 2.0])
+        lg = rng.choice(vals[: int(rng.integers(1, 6))], size=(w.T, w.E)).astype(np.float32)
+        if mode == "ulps":
+            steps = rng.integers(0, 3, size=(w.T, w.E)).astype(np.int32)
+            lg = (lg.view(np.int32) + np.where(lg >= 0, steps, -steps)).view(np.float32)
+    check(w, lg, with_recv_token=bool(case % 4))
+
+
+def _two_launch(w) -> bool:
+    cfg = ep.Config.of(w)
+    C = -(-w.T // 16)
+    return ep.route_layout_workspace_bytes(cfg) == -(-C * w.E // 256) * 256 + -(-C * w.R // 256) * 256 \
+        and w.T * w.k > 1024
+
+
+@pytest.mark.parametrize("T,k", [(33, 32), (47, 24), (63, 17), (65, 32), (129, 8), (4095, 8), (4096, 8)])
+def test_route_layout_column_and_block_edges(T, k):
+    # token counts around the 16-token columns and 64-token assign blocks,
+    # with enough picks to take the two-launch path
+    w = W.PREFILL.replace(name="edges", T=T, k=k, TG=8 if k > 8 else 4, m=2, seed=T * 100 + k)
+    assert _two_launch(w)
+    say("route_layout edges", w)
+    check(w, W.gen_logits(w))
+
+
+@pytest.mark.parametrize("w", [
+    W.Workload("fb_e96", T=333, H=128, E=96, G=4, TG=2, k=6, R=12, m=3, seed=41),     # general gate
+    W.Workload("fb_m4", T=200, H=128, E=256, G=8, TG=4, k=16, R=32, m=4, seed=42),    # m > 2
+    W.Workload("fb_r1024", T=70, H=128, E=1024, G=8, TG=2, k=8, R=1024, seed=43),     # ranks beyond one block
+    W.Workload("fb_e64", T=90, H=128, E=64, G=4, TG=2, k=4, R=8, seed=44),            # E < 128
+])
+def test_route_layout_fallback_shapes(w):
+    say("route_layout fallback", w)
+    check(w, W.gen_logits(w))
+
+
+def test_route_layout_zero_tokens():
+    w = W.PREFILL.replace(T=0)
+    cfg = ep.Config.of(w)
+    got = ep.route_layout(cfg, torch.empty((0, w.E), dtype=torch.float32, device="cuda"))
+    torch.cuda.synchronize()
+    assert to_host(got["cnt"]).sum() == 0 and to_host(got["off"]).tolist() == [0] * (w.E + 1)
+    assert to_host(got["ntok_rank"]).sum() == 0
