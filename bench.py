@@ -116,6 +116,9 @@ def parse():
                     help="CPU time of the oracle legs (half on one thread, half on all threads)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (for scaling HBM counters)")
+    ap.add_argument("--ceiling-probe", action="store_true",
+                    help="HBM rates of plain kernels (streaming read, write, copy; combine- and dispatch-shaped "
+                         "copies without their arithmetic) beside the library's dispatch and combine")
     return ap.parse_args()
 
 
@@ -157,6 +160,108 @@ def copy_probe():
     us, gbs = _copy_gbs(n)
     print(json.dumps({"kind": "copy_probe", "bytes_read": n, "bytes_written": n,
                       "us": round(us, 1), "gbs_read_plus_write": round(gbs, 1)}), flush=True)
+    return 0
+
+
+def ceiling_probe(args):
+    """What plain kernels reach on this GPU (libhbmprobe.so), as ceilings for
+    the dispatch and combine kernels: streaming (nt) read, write and copy
+    over 1 GiB, and copies with the combine's access pattern (a 16-byte piece
+    of each of a token's k rows gathered into one output piece) and the FP8
+    dispatch's payload pattern (a token's bf16 row stored to k rows of H
+    bytes), at the prefill shape, on the canonical layout's receive rows and
+    on sequential rows (t*k + j), beside ep_combine and ep_dispatch on the
+    same rows.  Each probe alternates between two copies of its buffers, so
+    every run reads from HBM; HIP events around `steps` runs."""
+    import numpy as np
+    import torch
+
+    import combine_group_limited_amd as ep
+    from combine_group_limited_amd import _lib as L
+    from combine_group_limited_amd import build as B
+    import workloads as W
+
+    if not os.path.exists(B.PROBE_LIB_PATH):
+        B.build()
+    P = ctypes.CDLL(B.PROBE_LIB_PATH)
+    vp, i, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+    P.hbm_probe_read.argtypes = [vp, sz, vp, vp]
+    P.hbm_probe_write.argtypes = [vp, sz, vp]
+    P.hbm_probe_copy.argtypes = [vp, vp, sz, vp]
+    P.hbm_probe_gather.argtypes = [vp, vp, vp, i, i, i, i, vp]
+    P.hbm_probe_scatter.argtypes = [vp, vp, vp, i, i, i, i, vp]
+    lib = L.lib()
+    dev = torch.device("cuda", 0)
+    sh = int(torch.cuda.current_stream().cuda_stream)
+    w = W.PREFILL
+    cfg = ep.Config.of(w)
+    c = cfg.c()
+    cp = ctypes.byref(c)
+    GiB = 1 << 30
+    big = [torch.empty(GiB, dtype=torch.uint8, device=dev) for _ in range(4)]
+    for t in big:
+        t.fill_(1)
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    lay = ep.route_layout(cfg, torch.from_numpy(W.gen_logits(w)).to(dev))
+    slot = lay["slot"]
+    seq = torch.arange(w.nrows, dtype=torch.int32, device=dev).view(w.T, w.k)
+    y = [torch.from_numpy(W.gen_y(w).view(np.int16)).view(torch.bfloat16).to(dev) for _ in range(2)]
+    x = [torch.from_numpy(W.gen_x(w).view(np.int16)).view(torch.bfloat16).to(dev) for _ in range(2)]
+    out = [torch.empty((w.T, w.H), dtype=torch.bfloat16, device=dev) for _ in range(2)]
+    recv = [torch.empty((w.nrows, w.H), dtype=torch.uint8, device=dev) for _ in range(2)]
+    sc = [torch.empty((w.nrows, w.H // 128), dtype=torch.float32, device=dev) for _ in range(2)]
+    torch.cuda.synchronize()
+    hev = HipEvents()
+    n = max(args.steps, 2)
+
+    def timed(fn):
+        for j in range(2):
+            if fn(j) != 0:
+                raise RuntimeError("probe launch failed")
+        e = hev.create(2)
+        hev.record(e[0], sh)
+        for j in range(n):
+            fn(j)
+        hev.record(e[1], sh)
+        t = hev.seconds(e[0], e[1]) / n
+        hev.destroy(e)
+        return t
+
+    gather_b = w.T * (2 * w.k * w.H + 2 * w.H + 4 * w.k)
+    scatter_b = w.T * (2 * w.H + w.k * w.H + 4 * w.k)
+    probes = {
+        "read_1GiB": (GiB, lambda j: P.hbm_probe_read(big[j % 2].data_ptr(), GiB, sink.data_ptr(), sh)),
+        "write_1GiB": (GiB, lambda j: P.hbm_probe_write(big[j % 2].data_ptr(), GiB, sh)),
+        "copy_1GiB": (2 * GiB, lambda j: P.hbm_probe_copy(big[j % 2].data_ptr(), big[2 + j % 2].data_ptr(), GiB, sh)),
+        "gather_layout_rows": (gather_b, lambda j: P.hbm_probe_gather(y[j % 2].data_ptr(), slot.data_ptr(),
+                                                                      out[j % 2].data_ptr(), w.T, w.H, w.k, w.nrows, sh)),
+        "gather_sequential_rows": (gather_b, lambda j: P.hbm_probe_gather(y[j % 2].data_ptr(), seq.data_ptr(),
+                                                                          out[j % 2].data_ptr(), w.T, w.H, w.k,
+                                                                          w.nrows, sh)),
+        "combine_layout_rows": (w.bytes_combine(), lambda j: lib.ep_combine(cp, y[j % 2].data_ptr(), slot.data_ptr(),
+                                                                           lay["w"].data_ptr(), out[j % 2].data_ptr(),
+                                                                           sh)),
+        "scatter_layout_rows": (scatter_b, lambda j: P.hbm_probe_scatter(x[j % 2].data_ptr(), slot.data_ptr(),
+                                                                         recv[j % 2].data_ptr(), w.T, w.H, w.k,
+                                                                         w.nrows, sh)),
+        "scatter_sequential_rows": (scatter_b, lambda j: P.hbm_probe_scatter(x[j % 2].data_ptr(), seq.data_ptr(),
+                                                                             recv[j % 2].data_ptr(), w.T, w.H, w.k,
+                                                                             w.nrows, sh)),
+        "dispatch_fp8_layout_rows": (w.bytes_dispatch_fp8(),
+                                     lambda j: lib.ep_dispatch(cp, x[j % 2].data_ptr(), slot.data_ptr(),
+                                                               L.EP_RECV_FP8_E4M3, recv[j % 2].data_ptr(),
+                                                               sc[j % 2].data_ptr(), sh)),
+    }
+    res = {}
+    for name, (nbytes, fn) in probes.items():
+        t = timed(fn)
+        res[name] = {"us": round(t * 1e6, 2), "bytes": nbytes, "gbs": round(nbytes / t / 1e9, 1),
+                     "frac_of_8000": round(nbytes / t / 1e9 / HBM_PEAK_GBS, 4)}
+        print("probe %-26s %9.2f us %8.1f GB/s" % (name, t * 1e6, nbytes / t / 1e9), file=sys.stderr, flush=True)
+    print(json.dumps({"metric": "HBM ceiling probes (plain kernels) beside dispatch and combine, prefill shape",
+                      "unit": "GB/s", "peak": HBM_PEAK_GBS, "steps": n,
+                      "config": {"workload": w.name, "tokens": w.T, "hidden": w.H, "topk": w.k},
+                      "probes": res}), flush=True)
     return 0
 
 
@@ -708,6 +813,8 @@ def main():
         return 2
     if args.copy_probe:
         return copy_probe()
+    if args.ceiling_probe:
+        return ceiling_probe(args)
 
     import torch
     import workloads as W

@@ -17,6 +17,10 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(PKG, "_build")
 LIB_PATH = os.path.join(PKG, "libep.so")
+# HBM bandwidth probes used by the benchmark's ceiling probe (not part of
+# the library's ABI)
+PROBE_LIB_PATH = os.path.join(PKG, "libhbmprobe.so")
+PROBE_SOURCES = ["probe.hip"]
 # content hash of the sources and flags the library was built from, written
 # next to it by build(); the loader compares it with the current sources
 HASH_PATH = LIB_PATH + ".sources"
@@ -46,7 +50,7 @@ HIPFLAGS = [
 
 
 def _inputs():
-    return [os.path.join(CSRC, f) for f in SOURCES + HEADERS] + [os.path.join(INCLUDE, "ep.h")]
+    return [os.path.join(CSRC, f) for f in SOURCES + PROBE_SOURCES + HEADERS] + [os.path.join(INCLUDE, "ep.h")]
 
 
 def source_hash(inputs=None) -> str:
@@ -75,7 +79,8 @@ def is_stale() -> bool:
     """True when libep.so is missing or was built from other sources or
     flags than the current ones (compared by content, not by time stamps,
     which a copied tree need not keep)."""
-    return not os.path.exists(LIB_PATH) or built_hash() != source_hash()
+    return (not os.path.exists(LIB_PATH) or not os.path.exists(PROBE_LIB_PATH)
+            or built_hash() != source_hash())
 
 
 def hipcc_available() -> bool:
@@ -97,18 +102,20 @@ def _compile(src: str) -> str:
 
 
 def build(verbose: bool = False) -> str:
-    """Compile every HIP source and link libep.so next to this file."""
+    """Compile every HIP source and link libep.so (and the benchmark's
+    libhbmprobe.so) next to this file."""
     os.makedirs(BUILD_DIR, exist_ok=True)
     digest = source_hash()
-    srcs = [os.path.join(CSRC, f) for f in SOURCES]
+    srcs = [os.path.join(CSRC, f) for f in SOURCES + PROBE_SOURCES]
     with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
         objs = list(ex.map(_compile, srcs))
-    tmp = LIB_PATH + ".tmp%d" % os.getpid()
-    cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs]
-    r = subprocess.run(cmd, capture_output=True, text=True)
-    if r.returncode != 0:
-        raise RuntimeError("link failed:\n%s\n%s" % (" ".join(cmd), r.stderr))
-    os.replace(tmp, LIB_PATH)
+    for path, part in ((LIB_PATH, objs[:len(SOURCES)]), (PROBE_LIB_PATH, objs[len(SOURCES):])):
+        tmp = path + ".tmp%d" % os.getpid()
+        cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *part]
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError("link failed:\n%s\n%s" % (" ".join(cmd), r.stderr))
+        os.replace(tmp, path)
     tmp = HASH_PATH + ".tmp%d" % os.getpid()
     with open(tmp, "w") as f:
         f.write(digest + "\n")
