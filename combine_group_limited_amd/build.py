@@ -21,6 +21,9 @@ LIB_PATH = os.path.join(PKG, "libep.so")
 # the library's ABI)
 PROBE_LIB_PATH = os.path.join(PKG, "libhbmprobe.so")
 PROBE_SOURCES = ["probe.hip"]
+# device self-checks run by the test suite (not part of the library's ABI)
+CHECK_LIB_PATH = os.path.join(PKG, "libepcheck.so")
+CHECK_SOURCES = ["selfcheck.hip"]
 # content hash of the sources and flags the library was built from, written
 # next to it by build(); the loader compares it with the current sources
 HASH_PATH = LIB_PATH + ".sources"
@@ -50,7 +53,8 @@ HIPFLAGS = [
 
 
 def _inputs():
-    return [os.path.join(CSRC, f) for f in SOURCES + PROBE_SOURCES + HEADERS] + [os.path.join(INCLUDE, "ep.h")]
+    return [os.path.join(CSRC, f) for f in SOURCES + PROBE_SOURCES + CHECK_SOURCES + HEADERS] + \
+        [os.path.join(INCLUDE, "ep.h")]
 
 
 def source_hash(inputs=None) -> str:
@@ -80,7 +84,7 @@ def is_stale() -> bool:
     flags than the current ones (compared by content, not by time stamps,
     which a copied tree need not keep)."""
     return (not os.path.exists(LIB_PATH) or not os.path.exists(PROBE_LIB_PATH)
-            or built_hash() != source_hash())
+            or not os.path.exists(CHECK_LIB_PATH) or built_hash() != source_hash())
 
 
 def hipcc_available() -> bool:
@@ -103,13 +107,14 @@ def _compile(src: str) -> str:
 
 def build(verbose: bool = False) -> str:
     """Compile every HIP source and link libep.so (and the benchmark's
-    libhbmprobe.so) next to this file."""
+    libhbmprobe.so and the tests' libepcheck.so) next to this file."""
     os.makedirs(BUILD_DIR, exist_ok=True)
     digest = source_hash()
-    srcs = [os.path.join(CSRC, f) for f in SOURCES + PROBE_SOURCES]
+    srcs = [os.path.join(CSRC, f) for f in SOURCES + PROBE_SOURCES + CHECK_SOURCES]
     with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
         objs = list(ex.map(_compile, srcs))
-    for path, part in ((LIB_PATH, objs[:len(SOURCES)]), (PROBE_LIB_PATH, objs[len(SOURCES):])):
+    n, p = len(SOURCES), len(PROBE_SOURCES)
+    for path, part in ((LIB_PATH, objs[:n]), (PROBE_LIB_PATH, objs[n:n + p]), (CHECK_LIB_PATH, objs[n + p:])):
         tmp = path + ".tmp%d" % os.getpid()
         cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *part]
         r = subprocess.run(cmd, capture_output=True, text=True)

@@ -87,6 +87,55 @@ __device__ __forceinline__ float cw_expf(float x) {
 
 __device__ __forceinline__ float sigmoid(float x) { return 1.0f / (1.0f + cw_expf(-x)); }
 
+// sigmoid(x) for |x| <= kSigmoidFastBound, bit-identical there to sigmoid()
+// in 17 instead of ~40 instructions.  Inside that range cw_expf's clamps and
+// special cases never apply; 2^n is applied with one ldexp, which is exact
+// because the result is a normal number (so it equals the two exact factor
+// multiplications); and 1 / y, y = 1 + exp(-x) in [1, 2^116), is v_rcp_f32
+// refined by one Newton step with fma.  That step gives the correctly rounded
+// quotient for every such y: checked on gfx950 against the IEEE division for
+// all 2,235,564,034 fp32 values with |x| <= 80.
+constexpr float kSigmoidFastBound = 80.0f;
+
+__device__ __forceinline__ float sigmoid_inrange(float x) {
+    const float L2E = 0x1.715476p+0f;
+    const float C1 = 0x1.62ep-1f;
+    const float C2 = 0x1.0bfbe8p-15f;
+    const float z = -x;
+    const float n = __builtin_rintf(z * L2E);
+    float r = __builtin_fmaf(-n, C1, z);
+    r = __builtin_fmaf(-n, C2, r);
+    float p = 0x1.a01a02p-13f;
+    p = __builtin_fmaf(p, r, 0x1.6c16c2p-10f);
+    p = __builtin_fmaf(p, r, 0x1.111112p-7f);
+    p = __builtin_fmaf(p, r, 0x1.555556p-5f);
+    p = __builtin_fmaf(p, r, 0x1.555556p-3f);
+    p = __builtin_fmaf(p, r, 0.5f);
+    p = __builtin_fmaf(p, r, 1.0f);
+    p = __builtin_fmaf(p, r, 1.0f);
+    const float y = 1.0f + __builtin_ldexpf(p, (int)n);
+    const float q = __builtin_amdgcn_rcpf(y);
+    return __builtin_fmaf(__builtin_fmaf(-y, q, 1.0f), q, q);
+}
+
+// In place: sigmoid of the N values one lane holds.  The short form runs
+// when every value of every active lane lies within kSigmoidFastBound (a
+// wave-uniform test, so only waves holding a value beyond it, or a NaN, take
+// the general form).
+template <int N>
+__device__ __forceinline__ void sigmoid_lane(float (&v)[N]) {
+    bool ok = true;
+#pragma unroll
+    for (int i = 0; i < N; ++i) ok = ok && __builtin_fabsf(v[i]) <= kSigmoidFastBound;
+    if (__all(ok)) {
+#pragma unroll
+        for (int i = 0; i < N; ++i) v[i] = sigmoid_inrange(v[i]);
+    } else {
+#pragma unroll
+        for (int i = 0; i < N; ++i) v[i] = sigmoid(v[i]);
+    }
+}
+
 // DPP lane permutations (gfx9 encodings).  Each pairs every lane with one
 // partner inside an aligned group of 2, 4, 8 or 16 lanes; used for
 // symmetric merges, where any pairing across the two halves of the group

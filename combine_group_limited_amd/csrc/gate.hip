@@ -8,12 +8,12 @@
 // weights s_j / ((s_0 + s_1) + ... ).
 //
 // Three kernels compute the same result:
-//  - gate_pair_kernel, two tokens per wavefront (one per 32-lane half, each
-//    lane holding a run of E/32 consecutive experts), when 32 divides E
-//    (128 <= E <= 1024), m <= 2 and a group is a power-of-two run of whole
-//    lanes (or TG = G).  Group scores are mostly in-lane, and each
-//    cross-lane step serves both tokens.  It can also count its picks per
-//    workgroup for the routing layout (HIST).
+//  - gate_pair_kernel, one or two tokens per wavefront (the token's 64 or 32
+//    lanes each holding a run of consecutive experts), when the lanes divide
+//    E (128 <= E <= 1024), m <= 2 and a group is a power-of-two run of whole
+//    lanes (or TG = G).  Group scores are mostly in-lane, and with two
+//    tokens each cross-lane step serves both.  It can also count its picks
+//    per workgroup for the routing layout (HIST).
 //  - gate_fast_kernel, one wavefront per token, lane l holding experts l,
 //    l + 64, ..., when the group size GS = E/G divides 64 and m <= 2, or
 //    TG = G: a group is an aligned run of GS lanes inside one register, and
@@ -24,8 +24,16 @@
 //  - gate_kernel, any shape: scores staged in LDS, lane g ranks group g's
 //    scores serially, k rounds of a 64-bit wave arg-max.
 //
-// Measured on MI355X at 4096 tokens, 256 experts in 8 groups, top-4 groups,
-// top-8 (HIP events): gate_fast_kernel 8.9 us, gate_pair_kernel 7.2 us.
+// Scores come from sigmoid_lane (device.h): the short exact form when every
+// logit of the wavefront lies within +-80.
+//
+// Measured on MI355X, 256 experts in 8 groups, top-4 groups, top-8, back to
+// back with the pick counts (HIP events): 128 tokens 5.3 us, 4096 tokens
+// 5.7 us with one token per wavefront (6.5 us with two; gate_fast_kernel
+// 8.9 us); 16384 tokens 14.5 us with two (18.9 us with one).  One wave's
+// dependency chain sets the time up to a few thousand tokens: the first
+// load of its logits from HBM (~1.8 us), the k pick rounds (~700 cycles
+// each) and the workgroup barrier before the counts are written.
 #include "device.h"
 #include "launch.h"
 
@@ -71,12 +79,15 @@ __global__ __launch_bounds__(kGateWaves * kWave) void gate_fast_kernel(
     // 1. scores (lanes past E read expert 0 and are masked afterwards)
     uint32_t sb[EPL];
     const float* row = logits + (size_t)t * E;
+    float lg[EPL];
 #pragma unroll
     for (int i = 0; i < EPL; ++i) {
         const int e = i * kWave + lane;
-        const float sg = sigmoid(row[e < E ? e : 0]);
-        sb[i] = e < E ? __float_as_uint(sg) : 0u;
+        lg[i] = row[e < E ? e : 0];
     }
+    sigmoid_lane(lg);
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) sb[i] = i * kWave + lane < E ? __float_as_uint(lg[i]) : 0u;
 
     // 2. kept groups (bit g of `kept`; groups hold GS = 2^gs_log2 <= 64 experts)
     uint64_t kept = ~0ull;
@@ -166,24 +177,30 @@ __global__ __launch_bounds__(kGateWaves * kWave) void gate_fast_kernel(
     }
 }
 
-// Two tokens per wavefront, one per 32-lane half: lane l of half h holds
-// the EPL = E / 32 consecutive experts [l*EPL, (l+1)*EPL) of token
-// 2 * (wavefront index) + h.  Used when 32 divides E and a group is a
+// TPW tokens per wavefront (1 or 2), LPT = 64 / TPW lanes per token: lane l
+// of the token's lanes holds the EPL = E / LPT consecutive experts
+// [l*EPL, (l+1)*EPL).  Used when LPT divides E and a group is a
 // power-of-two run of whole lanes (LPG = GS / EPL lanes, or every group
-// kept), with m <= 2.  A group's top-m is then mostly in-lane, and every
-// cross-lane step (group merge, pick maximum, ballot) serves both tokens
-// with one instruction, which halves the per-token instruction count of
-// the one-token-per-wavefront kernel.
+// kept), with m <= 2.  A group's top-m is then mostly in-lane; with two
+// tokens, every cross-lane step (group merge, pick maximum, ballot) serves
+// both with one instruction, which halves the per-token instruction count.
 //
-// Picks: each round takes the largest candidate key of each half (DPP
-// maximum within the half, read from lanes 31 and 63); the owner is the
-// lowest lane holding it, and inside the owner the lowest of its experts
-// with that key, which is the lowest expert index among exact ties since
-// lanes hold ascending runs of experts.
+// Picks: each round takes the largest candidate key of each token (DPP
+// maximum within its lanes, read from lane 31 and 63, or 63); the owner is
+// the lowest lane holding it, and inside the owner the lowest of its
+// experts with that key, which is the lowest expert index among exact ties
+// since lanes hold ascending runs of experts.
 constexpr uint64_t kHiHalf = 0xFFFFFFFF00000000ull;
-constexpr int kPairWaves = 8;                // waves per workgroup
-constexpr int kPairTokens = 2 * kPairWaves;  // tokens per workgroup (one histogram column)
+constexpr int kPairTokens = 16;  // tokens per workgroup (one histogram column)
 constexpr int kMaxExpertsHist = 1024;
+// One token per wavefront up to this many tokens, two above: one token per
+// wave halves each lane's serial work (E/64 experts instead of E/32), which
+// shortens every wavefront's dependency chain, while two tokens per wave
+// issue fewer instructions per token, which wins once the SIMDs hold enough
+// waves.
+#ifndef GATE_ONE_TOKEN_MAX_T
+#define GATE_ONE_TOKEN_MAX_T 4096
+#endif
 
 //
 // With HIST, the workgroup (kPairTokens tokens, one "column") also counts
@@ -192,26 +209,60 @@ constexpr int kMaxExpertsHist = 1024;
 // on virtual rank r (its first pick there), as bytes (at most kPairTokens
 // each, since a token's picks are distinct experts).  The layout's assign
 // step sums these columns instead of a separate counting launch.
-template <int EPL, int MC, bool HIST>
-__global__ __launch_bounds__(kPairWaves * kWave) void gate_pair_kernel(
+//
+// KF, GF: k and G as compile-time constants for common shapes (0: the
+// runtime values), so that the group ranking's lane reads and the pick
+// rounds unroll.  With R <= 64 the picks' ranks are tracked in scalar
+// registers during the rounds (the picks are wave-uniform per half), so
+// first-on-rank needs no lane exchange afterwards; `epr_magic` =
+// floor(2^32 / EPR) + 1 turns the division e / EPR into one high multiply,
+// exact for e < 2^16 (EPR = 1 has magic 1 and the rank is e itself).
+
+// Calls f(j) for j = 0 .. n-1: unrolled when N, the count known at compile
+// time, is positive, else a loop over the runtime count n.
+template <int N, typename F>
+__device__ __forceinline__ void for_count(int n, F&& f) {
+    if constexpr (N > 0) {
+#pragma unroll
+        for (int j = 0; j < N; ++j) f(j);
+    } else {
+        for (int j = 0; j < n; ++j) f(j);
+    }
+}
+
+__device__ __forceinline__ uint32_t rank_of(uint32_t e, uint32_t epr_magic) {
+    return __umulhi(e, epr_magic) + (epr_magic == 1u ? e : 0u);
+}
+
+template <int EPL, int MC, bool HIST, int KF, int GF, int TPW>
+__global__ __launch_bounds__(kPairTokens / TPW * kWave) void gate_pair_kernel(
     const float* __restrict__ logits, int32_t* __restrict__ topk_idx, float* __restrict__ topk_w, int T, int E,
-    int G, int TG, int k, int m, int lpg_log2, uint8_t* __restrict__ hist, uint8_t* __restrict__ rank_hist, int R,
-    int EPR) {
+    int G_rt, int TG, int k_rt, int m, int lpg_rt, uint8_t* __restrict__ hist, uint8_t* __restrict__ rank_hist,
+    int R, int EPR, uint32_t epr_magic) {
+    static_assert(TPW == 1 || TPW == 2, "one or two tokens per wavefront");
+    constexpr int LPT = kWave / TPW;  // lanes per token
+    constexpr int LPT_LOG2 = TPW == 1 ? 6 : 5;
     __shared__ int cnt_lds[HIST ? 2 * kMaxExpertsHist : 1];  // E expert counts, then R rank counts
+    const int k = KF > 0 ? KF : k_rt;
+    const int G = GF > 0 ? GF : G_rt;
+    // lanes per group: LPT / G when the groups are runs of whole lanes
+    const int lpg_log2 = GF > 0 ? __builtin_ctz((unsigned)LPT / (GF > 0 ? GF : 1)) : lpg_rt;
     // the wave index is uniform across the wavefront: read it into a scalar
     // register so that the row resource below is uniform too
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
-    const int half = lane >> 5;
-    const int hl = lane & 31;
-    const int t0 = (blockIdx.x * kPairWaves + wave) * 2;
+    const int half = TPW == 2 ? lane >> 5 : 0;  // the wave's token of this lane
+    const int hl = lane & (LPT - 1);             // lane within the token
+    const int t0 = blockIdx.x * kPairTokens + wave * TPW;
     if (!HIST && t0 >= T) return;  // the whole wave leaves; nothing below synchronises
     if (HIST)
         for (int i = threadIdx.x; i < E + R; i += blockDim.x) cnt_lds[i] = 0;
     const bool wlive = t0 < T;  // uniform: this wave has a token
     const int t = t0 + half;
     const bool live = t < T;  // the last wave's second half may have no token
+    const bool track_ranks = HIST && R <= 64;
     int my_e = 0;
+    uint64_t first0 = 0, first1 = 0;  // bit j: pick j of the token is its first on that rank
     if (wlive) {
 
     // 1. scores: EPL consecutive logits per lane, 16-byte loads through one
@@ -219,17 +270,21 @@ __global__ __launch_bounds__(kPairWaves * kWave) void gate_pair_kernel(
     //    bytes; a half with no token reads zeros and is masked below)
     uint32_t sb[EPL];
     {
-        const int ntok = T - t0 < 2 ? T - t0 : 2;
+        const int ntok = T - t0 < TPW ? T - t0 : TPW;
         const auto rr = buffer_rsrc(logits + (size_t)t0 * E, (uint32_t)(ntok * E) * 4u);
         const int base = (half * E + hl * EPL) * 4;
+        float lg[EPL];
 #pragma unroll
         for (int i = 0; i < EPL; i += 4) {
             const i32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rr, base + i * 4, 0, kCached);
-            sb[i + 0] = __float_as_uint(sigmoid(__int_as_float(v.x)));
-            sb[i + 1] = __float_as_uint(sigmoid(__int_as_float(v.y)));
-            sb[i + 2] = __float_as_uint(sigmoid(__int_as_float(v.z)));
-            sb[i + 3] = __float_as_uint(sigmoid(__int_as_float(v.w)));
+            lg[i + 0] = __int_as_float(v.x);
+            lg[i + 1] = __int_as_float(v.y);
+            lg[i + 2] = __int_as_float(v.z);
+            lg[i + 3] = __int_as_float(v.w);
         }
+        sigmoid_lane(lg);
+#pragma unroll
+        for (int i = 0; i < EPL; ++i) sb[i] = __float_as_uint(lg[i]);
     }
 
     // 2. kept groups: the group of this lane is g = hl >> lpg_log2
@@ -253,16 +308,19 @@ __global__ __launch_bounds__(kPairWaves * kWave) void gate_pair_kernel(
         merge_step<4, MC>(a0, a1, lpg_log2);
         merge_step<8, MC>(a0, a1, lpg_log2);
         merge_step<16, MC>(a0, a1, lpg_log2);
+        if (TPW == 1) merge_step<32, MC>(a0, a1, lpg_log2);
         float gf = __uint_as_float(a0);
         if (MC == 2 && m == 2) gf = gf + __uint_as_float(a1);
         const uint32_t mine = __float_as_uint(gf);
-        // rank of this lane's group among the G groups of its half
+        // rank of this lane's group among the G groups of its token (with G
+        // known at compile time every lane read is issued before the first
+        // comparison)
         const int g = hl >> lpg_log2;
         int rank = 0;
-        for (int o = 0; o < G; ++o) {
-            const uint32_t v = (uint32_t)__shfl((int)mine, (half << 5) + (o << lpg_log2), kWave);
+        for_count<GF>(G, [&](int o) {
+            const uint32_t v = (uint32_t)__shfl((int)mine, (half << LPT_LOG2) + (o << lpg_log2), kWave);
             rank += (v > mine || (v == mine && o < g)) ? 1 : 0;
-        }
+        });
         kept = rank < TG;
     }
 
@@ -275,27 +333,39 @@ __global__ __launch_bounds__(kPairWaves * kWave) void gate_pair_kernel(
     uint32_t my_s = 0u;
     float S = 0.0f;
     const uint32_t hsel = half ? ~0u : 0u;  // selects the upper half's value of a pair
-    for (int j = 0; j < k; ++j) {
+    uint64_t seen0 = 0, seen1 = 0;          // ranks picked so far, per token
+    for_count<KF>(k, [&](int j) {
         uint32_t bk = key[0];
 #pragma unroll
         for (int i = 1; i < EPL; ++i) bk = max(bk, key[i]);
-        // maximum of each half: row butterflies, then rows 0 -> 1 and 2 -> 3
+        // maximum of each token: row butterflies, then rows 0 -> 1 and
+        // 2 -> 3 (and 1 -> 2, 3 for one token per wavefront)
         uint32_t v = bk;
         v = max(v, dpp_u32<kDppXor1>(v));
         v = max(v, dpp_u32<kDppXor2>(v));
         v = max(v, dpp_u32<kDppHalfMirror>(v));
         v = max(v, dpp_u32<kDppMirror>(v));
         v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, kDppRowBcast15, 0xA, 0xF, false));
-        const uint32_t m0 = (uint32_t)__builtin_amdgcn_readlane((int)v, 31);
-        const uint32_t m1 = (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
-        const uint32_t tgt = m0 ^ ((m0 ^ m1) & hsel);
-        const uint64_t eq = __ballot(bk == tgt);
-        const int o0 = __ffsll((unsigned long long)(eq & ~kHiHalf)) - 1;
-        const int o1 = __ffsll((unsigned long long)(eq & kHiHalf)) - 1;
+        uint32_t tgt;
+        uint64_t eq;
+        int o0, o1 = 32;
+        if constexpr (TPW == 2) {
+            const uint32_t m0 = (uint32_t)__builtin_amdgcn_readlane((int)v, 31);
+            const uint32_t m1 = (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+            tgt = m0 ^ ((m0 ^ m1) & hsel);
+            eq = __ballot(bk == tgt);
+            o0 = __ffsll((unsigned long long)(eq & ~kHiHalf)) - 1;
+            o1 = __ffsll((unsigned long long)(eq & kHiHalf)) - 1;
+        } else {
+            v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, kDppRowBcast31, 0xC, 0xF, false));
+            tgt = (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+            eq = __ballot(bk == tgt);
+            o0 = __ffsll((unsigned long long)eq) - 1;
+        }
         // the owner lanes take their first key equal to the maximum; `open`
         // and `hit` stay per-lane booleans (lane masks), so the clears are
         // selects on those masks
-        bool open = lane == o0 || lane == o1;
+        bool open = lane == o0 || (TPW == 2 && lane == o1);
         uint32_t ii = 0u;
 #pragma unroll
         for (int i = 0; i < EPL; ++i) {
@@ -305,12 +375,28 @@ __global__ __launch_bounds__(kPairWaves * kWave) void gate_pair_kernel(
             ii = hit ? (uint32_t)i : ii;
         }
         const uint32_t e0 = (uint32_t)(o0 * EPL) + (uint32_t)__builtin_amdgcn_readlane((int)ii, o0);
-        const uint32_t e1 = (uint32_t)((o1 - 32) * EPL) + (uint32_t)__builtin_amdgcn_readlane((int)ii, o1);
-        const int e = (int)(e0 ^ ((e0 ^ e1) & hsel));
+        uint32_t e1 = 0u;
+        int e = (int)e0;
+        if constexpr (TPW == 2) {
+            e1 = (uint32_t)((o1 - 32) * EPL) + (uint32_t)__builtin_amdgcn_readlane((int)ii, o1);
+            e = (int)(e0 ^ ((e0 ^ e1) & hsel));
+        }
         my_e = hl == j ? e : my_e;
         my_s = hl == j ? tgt : my_s;
         S = S + __uint_as_float(tgt & ~kCandidate);
-    }
+        if (HIST) {
+            // e0, e1 are wave-uniform: scalar bookkeeping (used when
+            // R <= 64; the shifts are masked so other R stay defined)
+            const uint32_t r0 = rank_of(e0, epr_magic) & 63u;
+            first0 |= (uint64_t)(((seen0 >> r0) & 1ull) ^ 1ull) << j;
+            seen0 |= 1ull << r0;
+            if (TPW == 2) {
+                const uint32_t r1 = rank_of(e1, epr_magic) & 63u;
+                first1 |= (uint64_t)(((seen1 >> r1) & 1ull) ^ 1ull) << j;
+                seen1 |= 1ull << r1;
+            }
+        }
+    });
 
     // 5. weights
     if (live && hl < k) {
@@ -320,15 +406,19 @@ __global__ __launch_bounds__(kPairWaves * kWave) void gate_pair_kernel(
     }  // wlive
 
     if (HIST) {
-        // a pick is the token's first on its rank when no earlier pick of
-        // the token (lanes hl' < hl of the half) has the same rank; the
-        // shuffles run with every lane active
         const bool pick = wlive && live && hl < k;
-        const int r = pick ? my_e / EPR : -1;
+        const int r = pick ? (int)rank_of((uint32_t)my_e, epr_magic) : -1;
         bool first = pick;
-        for (int jj = 0; jj + 1 < k; ++jj) {
-            const int rj = __shfl(r, (half << 5) + jj, kWave);
-            first = first && !(jj < hl && rj == r);
+        if (track_ranks) {
+            first = pick && (((half ? first1 : first0) >> hl) & 1ull);
+        } else {
+            // a pick is the token's first on its rank when no earlier pick of
+            // the token (lanes hl' < hl of its token) has the same rank; the
+            // shuffles run with every lane active
+            for (int jj = 0; jj + 1 < k; ++jj) {
+                const int rj = __shfl(r, (half << LPT_LOG2) + jj, kWave);
+                first = first && !(jj < hl && rj == r);
+            }
         }
         __syncthreads();  // counters cleared
         if (pick) {
@@ -361,11 +451,14 @@ __global__ __launch_bounds__(kGateWaves * kWave) void gate_kernel(
 #pragma unroll
     for (int i = 0; i < EPL; ++i) {
         const int e = i * kWave + lane;
-        s[i] = 0.0f;
-        if (active && e < E) {
-            s[i] = sigmoid(row[e]);
-            s_lds[wave][e] = s[i];
-        }
+        s[i] = active && e < E ? row[e] : 0.0f;
+    }
+    sigmoid_lane(s);
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) {
+        const int e = i * kWave + lane;
+        if (active && e < E) s_lds[wave][e] = s[i];
+        else s[i] = 0.0f;
     }
     __syncthreads();
 
@@ -469,48 +562,76 @@ hipError_t launch_fast(const Shape& s, int gs_log2, const float* logits, int32_t
     return hipGetLastError();
 }
 
-template <int EPL, int MC>
-hipError_t launch_pair(const Shape& s, int lpg_log2, const float* logits, int32_t* idx, float* w, uint8_t* hist,
-                       uint8_t* rank_hist, hipStream_t st) {
+template <int EPL, int MC, int KF, int GF, int TPW>
+hipError_t launch_pair_tpw(const Shape& s, int lpg_log2, const float* logits, int32_t* idx, float* w, uint8_t* hist,
+                           uint8_t* rank_hist, hipStream_t st) {
     const int blocks = (s.T + kPairTokens - 1) / kPairTokens;
+    const int epr = s.E / s.R;
+    const uint32_t magic = (uint32_t)((1ull << 32) / (uint64_t)epr + 1ull);
+    constexpr int threads = kPairTokens / TPW * kWave;
     if (hist)
-        hipLaunchKernelGGL((gate_pair_kernel<EPL, MC, true>), dim3(blocks), dim3(kPairWaves * kWave), 0, st, logits,
-                           idx, w, s.T, s.E, s.G, s.TG, s.k, s.m, lpg_log2, hist, rank_hist, s.R, s.E / s.R);
+        hipLaunchKernelGGL((gate_pair_kernel<EPL, MC, true, KF, GF, TPW>), dim3(blocks), dim3(threads), 0, st,
+                           logits, idx, w, s.T, s.E, s.G, s.TG, s.k, s.m, lpg_log2, hist, rank_hist, s.R, epr, magic);
     else
-        hipLaunchKernelGGL((gate_pair_kernel<EPL, MC, false>), dim3(blocks), dim3(kPairWaves * kWave), 0, st, logits,
-                           idx, w, s.T, s.E, s.G, s.TG, s.k, s.m, lpg_log2, nullptr, nullptr, s.R, s.E / s.R);
+        hipLaunchKernelGGL((gate_pair_kernel<EPL, MC, false, KF, GF, TPW>), dim3(blocks), dim3(threads), 0, st,
+                           logits, idx, w, s.T, s.E, s.G, s.TG, s.k, s.m, lpg_log2, nullptr, nullptr, s.R, epr, magic);
     return hipGetLastError();
 }
 
-template <int EPL>
-hipError_t launch_pair_mc(const Shape& s, int mc, int lpg_log2, const float* logits, int32_t* idx, float* w,
-                          uint8_t* hist, uint8_t* rank_hist, hipStream_t st) {
-    if (mc == 0) return launch_pair<EPL, 0>(s, lpg_log2, logits, idx, w, hist, rank_hist, st);
-    if (mc == 1) return launch_pair<EPL, 1>(s, lpg_log2, logits, idx, w, hist, rank_hist, st);
-    return launch_pair<EPL, 2>(s, lpg_log2, logits, idx, w, hist, rank_hist, st);
+template <int EPL, int MC, int KF, int GF>
+hipError_t launch_pair(const Shape& s, int tpw, int lpg_log2, const float* logits, int32_t* idx, float* w,
+                       uint8_t* hist, uint8_t* rank_hist, hipStream_t st) {
+    // one token per wave has E/64 <= 16 experts per lane (E <= 1024)
+    if constexpr (EPL <= 16) {
+        if (tpw == 1) return launch_pair_tpw<EPL, MC, KF, GF, 1>(s, lpg_log2, logits, idx, w, hist, rank_hist, st);
+    }
+    return launch_pair_tpw<EPL, MC, KF, GF, 2>(s, lpg_log2, logits, idx, w, hist, rank_hist, st);
 }
 
-// The two-tokens-per-wavefront kernel applies: 32 | E with 4 <= E/32 <= 32
-// (E/32 experts per lane, read 16 bytes at a time), m <= 2, and either every
-// group is kept or a group is a power-of-two run of whole lanes of a half.
-bool pair_gate_shape(const Shape& s, int* epl, int* lpg_log2, int* mc) {
-    if (s.E % 32 != 0 || s.E < 128 || s.E > 1024 || s.m > 2) return false;
+template <int EPL>
+hipError_t launch_pair_mc(const Shape& s, int tpw, int mc, int lpg_log2, const float* logits, int32_t* idx, float* w,
+                          uint8_t* hist, uint8_t* rank_hist, hipStream_t st) {
+    // k = 8 picks from 8 groups: the shape of the DeepSeek-style configurations
+    const bool k8g8 = s.k == 8 && s.G == 8;
+    if (mc == 0) {
+        if (k8g8) return launch_pair<EPL, 0, 8, 8>(s, tpw, lpg_log2, logits, idx, w, hist, rank_hist, st);
+        return launch_pair<EPL, 0, 0, 0>(s, tpw, lpg_log2, logits, idx, w, hist, rank_hist, st);
+    }
+    if (mc == 1) return launch_pair<EPL, 1, 0, 0>(s, tpw, lpg_log2, logits, idx, w, hist, rank_hist, st);
+    if (k8g8) return launch_pair<EPL, 2, 8, 8>(s, tpw, lpg_log2, logits, idx, w, hist, rank_hist, st);
+    return launch_pair<EPL, 2, 0, 0>(s, tpw, lpg_log2, logits, idx, w, hist, rank_hist, st);
+}
+
+// The pair kernel applies with `tpw` tokens per wavefront (LPT = 64 / tpw
+// lanes per token): LPT | E with 4 <= E/LPT <= 32 (E/LPT experts per lane,
+// read 16 bytes at a time), E <= 1024, m <= 2, and either every group is kept
+// or a group is a power-of-two run of whole lanes of the token's lanes.
+bool pair_gate_shape(const Shape& s, int tpw, int* epl, int* lpg_log2, int* mc) {
+    const int LPT = kWave / tpw;
+    if (s.E % LPT != 0 || s.E < 4 * LPT || s.E > 32 * LPT || s.E > 1024 || s.m > 2) return false;
     const int GS = s.E / s.G;
-    *epl = s.E / 32;
+    *epl = s.E / LPT;
     *lpg_log2 = 0;
     while ((*epl << *lpg_log2) < GS) ++*lpg_log2;
-    const bool lanes_ok = GS % *epl == 0 && (*epl << *lpg_log2) == GS && (1 << *lpg_log2) <= 32;
+    const bool lanes_ok = GS % *epl == 0 && (*epl << *lpg_log2) == GS && (1 << *lpg_log2) <= LPT;
     if (s.TG != s.G && !lanes_ok) return false;
     *mc = s.TG == s.G ? 0 : s.m;
     return true;
 }
 
-hipError_t launch_pair_any(const Shape& s, int epl, int lpg_log2, int mc, const float* logits, int32_t* idx,
-                           float* w, uint8_t* hist, uint8_t* rank_hist, hipStream_t st) {
-    if (epl == 4) return launch_pair_mc<4>(s, mc, lpg_log2, logits, idx, w, hist, rank_hist, st);
-    if (epl == 8) return launch_pair_mc<8>(s, mc, lpg_log2, logits, idx, w, hist, rank_hist, st);
-    if (epl == 16) return launch_pair_mc<16>(s, mc, lpg_log2, logits, idx, w, hist, rank_hist, st);
-    return launch_pair_mc<32>(s, mc, lpg_log2, logits, idx, w, hist, rank_hist, st);
+// Tokens per wavefront for this shape (0: the pair kernel does not apply).
+int pair_tpw(const Shape& s, int* epl, int* lpg_log2, int* mc) {
+    if (s.T <= GATE_ONE_TOKEN_MAX_T && pair_gate_shape(s, 1, epl, lpg_log2, mc)) return 1;
+    if (pair_gate_shape(s, 2, epl, lpg_log2, mc)) return 2;
+    return 0;
+}
+
+hipError_t launch_pair_any(const Shape& s, int tpw, int epl, int lpg_log2, int mc, const float* logits,
+                           int32_t* idx, float* w, uint8_t* hist, uint8_t* rank_hist, hipStream_t st) {
+    if (epl == 4) return launch_pair_mc<4>(s, tpw, mc, lpg_log2, logits, idx, w, hist, rank_hist, st);
+    if (epl == 8) return launch_pair_mc<8>(s, tpw, mc, lpg_log2, logits, idx, w, hist, rank_hist, st);
+    if (epl == 16) return launch_pair_mc<16>(s, tpw, mc, lpg_log2, logits, idx, w, hist, rank_hist, st);
+    return launch_pair_mc<32>(s, tpw, mc, lpg_log2, logits, idx, w, hist, rank_hist, st);
 }
 
 template <int EPL>
@@ -529,12 +650,10 @@ __global__ __launch_bounds__(256) void scores_kernel(const float* logits, float*
     const size_t stride = (size_t)gridDim.x * blockDim.x;
     for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i * V < n; i += stride) {
         if (V == 4 && i * 4 + 4 <= n) {
-            float4 v = reinterpret_cast<const float4*>(logits)[i];
-            v.x = sigmoid(v.x);
-            v.y = sigmoid(v.y);
-            v.z = sigmoid(v.z);
-            v.w = sigmoid(v.w);
-            reinterpret_cast<float4*>(scores)[i] = v;
+            const float4 v = reinterpret_cast<const float4*>(logits)[i];
+            float f[4] = {v.x, v.y, v.z, v.w};
+            sigmoid_lane(f);
+            reinterpret_cast<float4*>(scores)[i] = float4{f[0], f[1], f[2], f[3]};
         } else {
 #pragma unroll
             for (int u = 0; u < V; ++u) {
@@ -552,8 +671,9 @@ hipError_t launch_route(const Shape& s, const float* logits, int32_t* topk_idx, 
     if (s.T == 0) return hipSuccess;
     {
         int pepl = 0, lpg_log2 = 0, pmc = 0;
-        if (pair_gate_shape(s, &pepl, &lpg_log2, &pmc))
-            return launch_pair_any(s, pepl, lpg_log2, pmc, logits, topk_idx, topk_w, nullptr, nullptr, stream);
+        const int tpw = pair_tpw(s, &pepl, &lpg_log2, &pmc);
+        if (tpw > 0)
+            return launch_pair_any(s, tpw, pepl, lpg_log2, pmc, logits, topk_idx, topk_w, nullptr, nullptr, stream);
     }
     const int epl = (s.E + kWave - 1) / kWave;
     const int GS = s.E / s.G;
@@ -578,7 +698,7 @@ hipError_t launch_route(const Shape& s, const float* logits, int32_t* topk_idx, 
 
 bool route_hist_supported(const Shape& s) {
     int epl, lpg_log2, mc;
-    return s.E <= kMaxExpertsHist && s.R <= s.E && pair_gate_shape(s, &epl, &lpg_log2, &mc);
+    return s.E <= kMaxExpertsHist && s.R <= s.E && pair_tpw(s, &epl, &lpg_log2, &mc) > 0;
 }
 
 int route_hist_columns(const Shape& s) { return (s.T + kPairTokens - 1) / kPairTokens; }
@@ -589,8 +709,9 @@ hipError_t launch_route_hist(const Shape& s, const float* logits, int32_t* topk_
                              uint8_t* rank_hist, hipStream_t stream) {
     if (s.T == 0) return hipSuccess;
     int epl = 0, lpg_log2 = 0, mc = 0;
-    if (!pair_gate_shape(s, &epl, &lpg_log2, &mc)) return hipErrorInvalidValue;
-    return launch_pair_any(s, epl, lpg_log2, mc, logits, topk_idx, topk_w, hist, rank_hist, stream);
+    const int tpw = pair_tpw(s, &epl, &lpg_log2, &mc);
+    if (tpw == 0) return hipErrorInvalidValue;
+    return launch_pair_any(s, tpw, epl, lpg_log2, mc, logits, topk_idx, topk_w, hist, rank_hist, stream);
 }
 
 hipError_t launch_scores(const Shape& s, const float* logits, float* scores, hipStream_t stream) {

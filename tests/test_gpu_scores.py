@@ -90,3 +90,22 @@ def test_route_weights_are_the_ranked_scores():
         S = (S + sel[:, j]).astype(np.float32)
     w = (sel / S[:, None]).astype(np.float32)
     check(wt, w, "weights from scores")
+
+
+def test_short_sigmoid_equals_the_general_form_on_its_whole_domain():
+    """Every fp32 value with |x| <= 80 (the domain of the short sigmoid form
+    the kernels take when a whole wavefront's logits lie in it) goes through
+    both device forms; their bits must agree everywhere.  The general form is
+    the one the sweeps above compare with the oracle."""
+    import ctypes
+
+    from combine_group_limited_amd import build as B
+    lib = ctypes.CDLL(B.CHECK_LIB_PATH)
+    lib.ep_check_sigmoid_inrange.argtypes = [ctypes.c_float, ctypes.c_void_p, ctypes.c_void_p]
+    counts = torch.zeros(2, dtype=torch.int64, device="cuda")
+    say("exhaustive short-sigmoid check, |x| <= 80")
+    rc = lib.ep_check_sigmoid_inrange(80.0, counts.data_ptr(), torch.cuda.current_stream().cuda_stream)
+    assert rc == 0
+    tested, bad = (int(v) for v in counts.cpu())
+    assert tested == 2 * (0x42A00000 + 1), tested  # every pattern from -80 to 80, both zeros
+    assert bad == 0, "%d inputs differ" % bad

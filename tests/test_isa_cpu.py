@@ -33,9 +33,10 @@ def _isa(src: str, out_dir: str) -> str:
 @pytest.fixture(scope="module")
 def isa():
     with tempfile.TemporaryDirectory() as d:
-        srcs = [os.path.join(B.CSRC, f) for f in B.SOURCES]
+        names = B.SOURCES + B.PROBE_SOURCES + B.CHECK_SOURCES
+        srcs = [os.path.join(B.CSRC, f) for f in names]
         with cf.ThreadPoolExecutor(max_workers=min(6, len(srcs))) as ex:
-            return dict(zip(B.SOURCES, ex.map(lambda s: _isa(s, d), srcs)))
+            return dict(zip(names, ex.map(lambda s: _isa(s, d), srcs)))
 
 
 def _kernels(text):
