@@ -16,9 +16,11 @@ constexpr int kWave = 64;
 constexpr int kCached = 0;
 constexpr int kStream = 2;
 
-// Raw buffer resource over `bytes` bytes at `base`.  Accesses at or past
-// `bytes` read zero and drop stores, so each row gets its own resource and
-// an access can never leave its row.  Word 3 selects 32-bit raw data.
+// Raw buffer resource over `bytes` bytes at `base`, a GLOBAL memory address
+// (a buffer access addresses global memory, so a pointer into LDS must never
+// be passed here).  Accesses at or past `bytes` read zero and drop stores,
+// so each row gets its own resource and an access can never leave its row.
+// Word 3 selects 32-bit raw data.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
@@ -196,14 +198,21 @@ __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
     return v;
 }
 
-// Inclusive prefix sum across the wavefront.
+// Inclusive prefix sum across a fully active wavefront, with DPP: shifts by
+// 1, 2, 4 and 8 lanes within each 16-lane row (lanes shifted in from before
+// the row read 0), then row 0's total into row 1 and row 2's into row 3
+// (row_bcast:15), then row 1's into rows 2 and 3 (row_bcast:31).
+constexpr int kDppRowShr1 = 0x111;
+constexpr int kDppRowShr2 = 0x112;
+constexpr int kDppRowShr4 = 0x114;
+constexpr int kDppRowShr8 = 0x118;
 __device__ __forceinline__ int wave_inclusive_sum(int v) {
-    const int lane = threadIdx.x & (kWave - 1);
-#pragma unroll
-    for (int d = 1; d < kWave; d <<= 1) {
-        int o = __shfl_up(v, d, kWave);
-        if (lane >= d) v += o;
-    }
+    v += __builtin_amdgcn_update_dpp(0, v, kDppRowShr1, 0xF, 0xF, true);
+    v += __builtin_amdgcn_update_dpp(0, v, kDppRowShr2, 0xF, 0xF, true);
+    v += __builtin_amdgcn_update_dpp(0, v, kDppRowShr4, 0xF, 0xF, true);
+    v += __builtin_amdgcn_update_dpp(0, v, kDppRowShr8, 0xF, 0xF, true);
+    v += __builtin_amdgcn_update_dpp(0, v, kDppRowBcast15, 0xA, 0xF, false);
+    v += __builtin_amdgcn_update_dpp(0, v, kDppRowBcast31, 0xC, 0xF, false);
     return v;
 }
 

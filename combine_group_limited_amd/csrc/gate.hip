@@ -426,8 +426,13 @@ __global__ __launch_bounds__(kPairTokens / TPW * kWave) void gate_pair_kernel(
             if (first) atomicAdd(&cnt_lds[E + r], 1);
         }
         __syncthreads();
+        // whole dwords (four byte counts each), so every line of the column
+        // is written in full by this workgroup
         const size_t c = blockIdx.x;
-        for (int i = threadIdx.x; i < E; i += blockDim.x) hist[c * E + i] = (uint8_t)cnt_lds[i];
+        uint32_t* h32 = reinterpret_cast<uint32_t*>(hist + c * E);
+        for (int i = threadIdx.x; i < (E >> 2); i += blockDim.x)
+            h32[i] = (uint32_t)cnt_lds[4 * i] | ((uint32_t)cnt_lds[4 * i + 1] << 8) |
+                     ((uint32_t)cnt_lds[4 * i + 2] << 16) | ((uint32_t)cnt_lds[4 * i + 3] << 24);
         for (int i = threadIdx.x; i < R; i += blockDim.x) rank_hist[c * R + i] = (uint8_t)cnt_lds[E + i];
     }
 }
@@ -591,14 +596,16 @@ hipError_t launch_pair(const Shape& s, int tpw, int lpg_log2, const float* logit
 template <int EPL>
 hipError_t launch_pair_mc(const Shape& s, int tpw, int mc, int lpg_log2, const float* logits, int32_t* idx, float* w,
                           uint8_t* hist, uint8_t* rank_hist, hipStream_t st) {
-    // k = 8 picks from 8 groups: the shape of the DeepSeek-style configurations
-    const bool k8g8 = s.k == 8 && s.G == 8;
-    if (mc == 0) {
-        if (k8g8) return launch_pair<EPL, 0, 8, 8>(s, tpw, lpg_log2, logits, idx, w, hist, rank_hist, st);
-        return launch_pair<EPL, 0, 0, 0>(s, tpw, lpg_log2, logits, idx, w, hist, rank_hist, st);
+    // k = 8 picks from 8 groups with up to 8 experts per lane (up to 256 or
+    // 512 experts): the shape of the DeepSeek-style configurations.  (With
+    // more experts per lane the unrolled rounds run out of scalar registers.)
+    const bool k8g8 = EPL <= 8 && s.k == 8 && s.G == 8;
+    if constexpr (EPL <= 8) {
+        if (k8g8 && mc == 0) return launch_pair<EPL, 0, 8, 8>(s, tpw, lpg_log2, logits, idx, w, hist, rank_hist, st);
+        if (k8g8 && mc == 2) return launch_pair<EPL, 2, 8, 8>(s, tpw, lpg_log2, logits, idx, w, hist, rank_hist, st);
     }
+    if (mc == 0) return launch_pair<EPL, 0, 0, 0>(s, tpw, lpg_log2, logits, idx, w, hist, rank_hist, st);
     if (mc == 1) return launch_pair<EPL, 1, 0, 0>(s, tpw, lpg_log2, logits, idx, w, hist, rank_hist, st);
-    if (k8g8) return launch_pair<EPL, 2, 8, 8>(s, tpw, lpg_log2, logits, idx, w, hist, rank_hist, st);
     return launch_pair<EPL, 2, 0, 0>(s, tpw, lpg_log2, logits, idx, w, hist, rank_hist, st);
 }
 

@@ -189,11 +189,28 @@ __device__ void assign_pairs(int e, long p0, const int32_t* base, uint64_t* mask
     }
 }
 
-// expert id of pair p for the assign step: -1 if unrouted or p >= P
+// expert id of pair p for the assign step: -1 if unrouted or p >= P.
+// `idx` may point to global memory or to LDS (the one-workgroup kernel
+// stages the ids there), so this is a plain pointer load.
 __device__ __forceinline__ int pair_expert(const int32_t* __restrict__ idx, long p, long P, int E) {
     if (p >= P) return -1;
     const int v = idx[p];
     return (unsigned)v < (unsigned)E ? v : -1;
+}
+
+// expert id of pair p0 + threadIdx.x, `idx` in GLOBAL memory only (chunks of
+// at most 1024 pairs): -1 if unrouted or at or past P.  The load goes
+// through a buffer resource over the chunk's pairs below P (none when
+// P <= p0), so it is unconditional: no branch forces a wait on it before
+// the value is used, and nothing outside [p0, P) is read (lanes past it
+// read 0).  A buffer resource addresses global memory, so an LDS pointer
+// must never reach it.
+__device__ __forceinline__ int chunk_expert_global(const int32_t* __restrict__ idx, long p0, long P, int E) {
+    const long n = P - p0;
+    const uint32_t bytes = n <= 0 ? 0u : (uint32_t)(n < 1024 ? n : 1024) * 4u;
+    const auto rs = buffer_rsrc(n > 0 ? idx + p0 : idx, bytes);
+    const int v = __builtin_amdgcn_raw_buffer_load_b32(rs, (int)threadIdx.x * 4, 0, kCached);
+    return (long)threadIdx.x < n && (unsigned)v < (unsigned)E ? v : -1;
 }
 
 template <int W>
@@ -396,21 +413,23 @@ __global__ __launch_bounds__(W * 64) void layout_small_kernel(
     }
 }
 
-// column loads in flight per thread (added as packed bytes 15 at a time:
-// 15 * 16 < 256 keeps the byte sums exact)
-constexpr int kColBatch = 32;
+// 16-byte column loads in flight per thread, added as packed bytes (8 * 16
+// < 256 keeps the byte sums of a batch exact)
+constexpr int kColBatch = 8;
 
 // Layout from the routing step's per-column histograms (route_hist:
 // columns of CT tokens, hist [C][E] and rank_hist [C][R] bytes), in one
 // launch.  Block b takes the CB columns [b*CB, (b+1)*CB), i.e. the pairs of
 // tokens [b*CB*CT, (b+1)*CB*CT), in chunks of NT = W*64 pairs:
 //  1. per expert, the sum of all columns (its count) and of the columns
-//     before the block (its rows before the block).  A 4-byte load holds
-//     four experts' counts of one column; kColBatch loads are issued
-//     together and added as packed bytes, unpacked after every fifteen (a
-//     column count is at most CT = 16, so fifteen of them fit a byte).  Thread (g, d) sums
-//     dword d of the rows g, g + NG, ... (NG = NT / (E/4) row groups), then
-//     the groups meet in LDS.
+//     before the block (its rows before the block).  A 16-byte load holds
+//     sixteen experts' counts of one column; thread (g, d) reads piece d of
+//     the rows g, g + RG, ... (TPR = E/16 threads per row, RG = NT / TPR row
+//     groups), kColBatch loads at a time, adds them as packed bytes and
+//     unpacks each batch into 16-bit pairs (a column count is at most
+//     CT = 16, so a batch's sum fits a byte; a sum of all C <= 256 columns
+//     fits 16 bits).  The row groups inside a wavefront meet by lane
+//     exchanges, the W wavefronts in LDS.
 //  2. expert offsets by a block-wide scan; block 0 writes the counts,
 //     offsets and per-rank token counts.
 //  3. slots as in assign_pairs, chunk by chunk, carrying each expert's next
@@ -424,55 +443,70 @@ __global__ __launch_bounds__(W * 64) void layout_assign_cols_kernel(
     int CT) {
     extern __shared__ __align__(16) unsigned char ac_sm[];
     constexpr int NT = W * 64;
-    const int ED = E >> 2;   // dwords per histogram row
-    const int NG = NT / ED;  // row groups
     uint64_t* mask = reinterpret_cast<uint64_t*>(ac_sm);        // [W][E]
     int32_t* wpre = reinterpret_cast<int32_t*>(mask + W * E);    // [W][E]; expert totals before step 3
     int32_t* base = wpre + W * E;                                // [E]
-    int32_t* red = base + E;                                     // [2][NG][E]: sums before the block, all
-    int32_t* rtot = red + 2 * NG * E;                            // [R]
+    int32_t* red = base + E;                                     // [2][W][E]: sums before the block, all
+    int32_t* rtot = red + 2 * W * E;                             // [R]
     __shared__ int wsum[W];
     const int tid = threadIdx.x;
     const int c0 = blockIdx.x * CB;
     const long p_begin = (long)c0 * CT * k;
     const long p_end = min(P, (long)(c0 + CB) * CT * k);
-    int e_first = pair_expert(idx, p_begin + tid, p_end, E);
+    int e_first = chunk_expert_global(idx, p_begin, p_end, E);
 
     for (int i = tid; i < W * E; i += NT) mask[i] = 0ull;
     for (int i = tid; i < R; i += NT) rtot[i] = 0;
     {
-        // NG = NT / ED exactly, so every thread has a g < NG.  Loads go out
-        // kColBatch at a time (independent registers) and are added as
-        // packed bytes, 15 at a time (15 counts of at most CT = 16 fit a byte).
-        const int d = tid % ED, g = tid / ED;
-        const uint32_t* h32 = reinterpret_cast<const uint32_t*>(hist) + d;
-        int pre[4] = {0, 0, 0, 0}, all[4] = {0, 0, 0, 0};
-        for (int r0 = g; r0 < C; r0 += kColBatch * NG) {
-            uint32_t v[kColBatch];
+        const int TPR = E >> 4;     // threads per row (a power of two <= 64)
+        const int RG = NT / TPR;    // row groups
+        const int d = tid & (TPR - 1), g = tid / TPR;
+        const u32x4* h = reinterpret_cast<const u32x4*>(hist) + d;
+        uint32_t pp[8], pa[8];  // 16-bit count pairs: word 2q + h holds experts 4q + 2h (low), 4q + 2h + 1
+#pragma unroll
+        for (int i = 0; i < 8; ++i) pp[i] = pa[i] = 0u;
+        for (int r0 = g; r0 < C; r0 += kColBatch * RG) {
+            // unconditional loads (row clamped into [0, C), its value masked)
+            u32x4 v[kColBatch];
 #pragma unroll
             for (int u = 0; u < kColBatch; ++u) {
-                const int r = r0 + u * NG;
-                v[u] = r < C ? h32[(size_t)r * ED] : 0u;
+                const int r = r0 + u * RG;
+                v[u] = h[(size_t)(r < C ? r : C - 1) * TPR];
             }
-            uint32_t pp = 0u, pa = 0u;
+            u32x4 bp = u32x4{0, 0, 0, 0}, ba = u32x4{0, 0, 0, 0};  // packed byte sums of the batch
 #pragma unroll
             for (int u = 0; u < kColBatch; ++u) {
-                pa += v[u];
-                pp += (r0 + u * NG < c0) ? v[u] : 0u;
-                if (u % 15 == 14 || u == kColBatch - 1) {  // at most 15 packed counts per byte
+                const int r = r0 + u * RG;
+                const u32x4 z = u32x4{0, 0, 0, 0};
+                ba += r < C ? v[u] : z;
+                bp += r < c0 ? v[u] : z;  // c0 <= C
+            }
 #pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        pre[q] += (int)((pp >> (8 * q)) & 0xFFu);
-                        all[q] += (int)((pa >> (8 * q)) & 0xFFu);
-                    }
-                    pp = pa = 0u;
-                }
+            for (int q = 0; q < 4; ++q) {
+                pp[2 * q] += (bp[q] & 0xFFu) | ((bp[q] & 0xFF00u) << 8);
+                pp[2 * q + 1] += ((bp[q] >> 16) & 0xFFu) | ((bp[q] >> 8) & 0xFF0000u);
+                pa[2 * q] += (ba[q] & 0xFFu) | ((ba[q] & 0xFF00u) << 8);
+                pa[2 * q + 1] += ((ba[q] >> 16) & 0xFFu) | ((ba[q] >> 8) & 0xFF0000u);
             }
         }
+        // the 64 / TPR row groups of a wavefront: lanes d, d + TPR, ...
+        for (int D = TPR; D < kWave; D <<= 1) {
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            red[g * E + 4 * d + q] = pre[q];
-            red[(NG + g) * E + 4 * d + q] = all[q];
+            for (int i = 0; i < 8; ++i) {
+                pp[i] += (uint32_t)__shfl_xor((int)pp[i], D, kWave);
+                pa[i] += (uint32_t)__shfl_xor((int)pa[i], D, kWave);
+            }
+        }
+        if ((tid & (kWave - 1)) < TPR) {
+            const int wv = tid >> 6;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const int e = 16 * d + 2 * i;
+                red[wv * E + e] = (int)(pp[i] & 0xFFFFu);
+                red[wv * E + e + 1] = (int)(pp[i] >> 16);
+                red[(W + wv) * E + e] = (int)(pa[i] & 0xFFFFu);
+                red[(W + wv) * E + e + 1] = (int)(pa[i] >> 16);
+            }
         }
     }
     if (blockIdx.x == 0) {
@@ -497,9 +531,10 @@ __global__ __launch_bounds__(W * 64) void layout_assign_cols_kernel(
     __syncthreads();
     for (int e = tid; e < E; e += NT) {
         int before = 0, all = 0;
-        for (int g = 0; g < NG; ++g) {
+#pragma unroll
+        for (int g = 0; g < W; ++g) {
             before += red[g * E + e];
-            all += red[(NG + g) * E + e];
+            all += red[(W + g) * E + e];
         }
         base[e] = before;
         wpre[e] = all;
@@ -531,8 +566,9 @@ __global__ __launch_bounds__(W * 64) void layout_assign_cols_kernel(
     if (blockIdx.x == 0 && tid == 0) off[E] = total;
 
     for (long p0 = p_begin; p0 < p_end; p0 += NT) {
-        const int e = p0 == p_begin ? e_first : pair_expert(idx, p0 + tid, p_end, E);
+        const int e = p0 == p_begin ? e_first : chunk_expert_global(idx, p0, p_end, E);
         assign_pairs<W>(e, p0, base, mask, wpre, slot, recv_token, p_end, k, E, total);
+        if (p0 + NT >= p_end) break;  // (uniform) no next chunk
         __syncthreads();
         // the next chunk's rows start after this chunk's pairs
         for (int i = tid; i < E; i += NT) {
@@ -639,22 +675,22 @@ hipError_t launch_layout(const Shape& s, const int32_t* topk_idx, int32_t* cnt, 
 
 // Columns of the routing step's histograms per assign block (CB) and the
 // launch shape of layout_assign_cols_kernel; false if the shape does not
-// fit its limits (E/4 dwords per histogram row must divide the block, the
-// ranks must fit the block, and the LDS must fit 64 KiB).
+// fit its limits (E/16 threads per histogram row, a power of two <= 64; the
+// ranks must fit the block; the LDS must fit 64 KiB).
 namespace {
 constexpr int kColsPerAssignBlock = 4;
 constexpr size_t kColsMaxLds = 65536;
 
 size_t cols_lds_bytes(int W, int E, int R) {
-    const int NT = W * 64, NG = NT / (E / 4);
-    return (size_t)(12 * W + 4) * E + (size_t)2 * NG * E * 4 + (size_t)R * 4;
+    return (size_t)(12 * W + 4) * E + (size_t)2 * W * E * 4 + (size_t)R * 4;
 }
 }  // namespace
 
 bool layout_from_hist_supported(const Shape& s) {
     const int W = layout_waves(s.E);
     const int NT = W * 64;
-    if (s.E % 4 != 0 || s.E / 4 > NT || NT % (s.E / 4) != 0) return false;
+    const int tpr = s.E / 16;
+    if (s.E % 16 != 0 || tpr > 64 || (tpr & (tpr - 1)) != 0) return false;
     if (s.R > NT || NT % s.R != 0) return false;
     return cols_lds_bytes(W, s.E, s.R) <= kColsMaxLds;
 }
