@@ -198,6 +198,67 @@ __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
     return v;
 }
 
+// Sum of v over the lanes of a fully active wavefront that share lane % tpr
+// (tpr a power of two <= 64), in each of those lanes: DPP rotations by tpr,
+// 2 tpr, ... within each 16-lane row, then gfx950's row swaps.
+// v_permlane16_swap(v, v) returns rows (0, 0, 2, 2) and (1, 1, 3, 3) of v,
+// v_permlane32_swap(v, v) rows (0, 1, 0, 1) and (2, 3, 2, 3) (checked on the
+// device), so the sum of the two halves is the sum over row pairs.
+constexpr int kDppRowRor1 = 0x121;
+constexpr int kDppRowRor2 = 0x122;
+constexpr int kDppRowRor4 = 0x124;
+constexpr int kDppRowRor8 = 0x128;
+template <int TPR>
+__device__ __forceinline__ uint32_t lane_residue_sum(uint32_t v) {
+    if constexpr (TPR <= 1) v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, kDppRowRor1, 0xF, 0xF, true);
+    if constexpr (TPR <= 2) v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, kDppRowRor2, 0xF, 0xF, true);
+    if constexpr (TPR <= 4) v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, kDppRowRor4, 0xF, 0xF, true);
+    if constexpr (TPR <= 8) v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, kDppRowRor8, 0xF, 0xF, true);
+    if constexpr (TPR <= 16) {
+        const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+        v = r[0] + r[1];
+    }
+    if constexpr (TPR <= 32) {
+        const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+        v = r[0] + r[1];
+    }
+    return v;
+}
+
+// lane_residue_sum over the N words of a lane, with tpr (a power of two <=
+// 64) chosen at run time once for all of them
+template <int N>
+__device__ __forceinline__ void lane_residue_sums(uint32_t (&v)[N], int tpr) {
+    switch (tpr) {
+        case 1:
+#pragma unroll
+            for (int i = 0; i < N; ++i) v[i] = lane_residue_sum<1>(v[i]);
+            break;
+        case 2:
+#pragma unroll
+            for (int i = 0; i < N; ++i) v[i] = lane_residue_sum<2>(v[i]);
+            break;
+        case 4:
+#pragma unroll
+            for (int i = 0; i < N; ++i) v[i] = lane_residue_sum<4>(v[i]);
+            break;
+        case 8:
+#pragma unroll
+            for (int i = 0; i < N; ++i) v[i] = lane_residue_sum<8>(v[i]);
+            break;
+        case 16:
+#pragma unroll
+            for (int i = 0; i < N; ++i) v[i] = lane_residue_sum<16>(v[i]);
+            break;
+        case 32:
+#pragma unroll
+            for (int i = 0; i < N; ++i) v[i] = lane_residue_sum<32>(v[i]);
+            break;
+        default:
+            break;  // 64: one lane per residue
+    }
+}
+
 // Inclusive prefix sum across a fully active wavefront, with DPP: shifts by
 // 1, 2, 4 and 8 lanes within each 16-lane row (lanes shifted in from before
 // the row read 0), then row 0's total into row 1 and row 2's into row 3

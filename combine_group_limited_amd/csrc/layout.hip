@@ -416,6 +416,9 @@ __global__ __launch_bounds__(W * 64) void layout_small_kernel(
 // 16-byte column loads in flight per thread, added as packed bytes (8 * 16
 // < 256 keeps the byte sums of a batch exact)
 constexpr int kColBatch = 8;
+// rank-column loads of block 0 issued with the expert columns (the rows per
+// thread, C / (NT / R), at 256 columns of 32 ranks)
+constexpr int kRankBatch = 16;
 
 // Layout from the routing step's per-column histograms (route_hist:
 // columns of CT tokens, hist [C][E] and rank_hist [C][R] bytes), in one
@@ -454,6 +457,18 @@ __global__ __launch_bounds__(W * 64) void layout_assign_cols_kernel(
     const long p_begin = (long)c0 * CT * k;
     const long p_end = min(P, (long)(c0 + CB) * CT * k);
     int e_first = chunk_expert_global(idx, p_begin, p_end, E);
+    // block 0 also sums the rank columns (below); its first kRankBatch rows
+    // per thread are loaded here, unconditionally (rows clamped into range,
+    // C >= 1), so their latency overlaps the expert columns'
+    const int NR = NT / R, rr = tid % R, rg = tid / R;
+    uint32_t rv[kRankBatch];
+    if (blockIdx.x == 0) {
+#pragma unroll
+        for (int u = 0; u < kRankBatch; ++u) {
+            const int row = rg + u * NR;
+            rv[u] = rank_hist[(size_t)(row < C ? row : C - 1) * R + rr];
+        }
+    }
 
     for (int i = tid; i < W * E; i += NT) mask[i] = 0ull;
     for (int i = tid; i < R; i += NT) rtot[i] = 0;
@@ -490,13 +505,9 @@ __global__ __launch_bounds__(W * 64) void layout_assign_cols_kernel(
             }
         }
         // the 64 / TPR row groups of a wavefront: lanes d, d + TPR, ...
-        for (int D = TPR; D < kWave; D <<= 1) {
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                pp[i] += (uint32_t)__shfl_xor((int)pp[i], D, kWave);
-                pa[i] += (uint32_t)__shfl_xor((int)pa[i], D, kWave);
-            }
-        }
+        // (16-bit pair sums stay below 2^16, so packed adds are exact)
+        lane_residue_sums(pp, TPR);
+        lane_residue_sums(pa, TPR);
         if ((tid & (kWave - 1)) < TPR) {
             const int wv = tid >> 6;
 #pragma unroll
@@ -510,21 +521,13 @@ __global__ __launch_bounds__(W * 64) void layout_assign_cols_kernel(
         }
     }
     if (blockIdx.x == 0) {
-        // tokens per rank: thread (g, r) sums byte r of the rows g, g + NR,
-        // ... (R divides NT, so every thread has a g < NR)
-        const int NR = NT / R;
-        const int rr = tid % R, g = tid / R;
+        // tokens per rank: thread (rg, rr) sums byte rr of the rows rg,
+        // rg + NR, ... (R divides NT, so every thread has an rg < NR); the
+        // first kRankBatch rows were loaded with the expert columns
         int acc = 0;
-        for (int r0 = g; r0 < C; r0 += kColBatch * NR) {
-            uint32_t v[kColBatch];  // issued together, like the expert columns
 #pragma unroll
-            for (int u = 0; u < kColBatch; ++u) {
-                const int row = r0 + u * NR;
-                v[u] = row < C ? rank_hist[(size_t)row * R + rr] : 0u;
-            }
-#pragma unroll
-            for (int u = 0; u < kColBatch; ++u) acc += (int)v[u];
-        }
+        for (int u = 0; u < kRankBatch; ++u) acc += rg + u * NR < C ? (int)rv[u] : 0;
+        for (int row = rg + kRankBatch * NR; row < C; row += NR) acc += (int)rank_hist[(size_t)row * R + rr];
         __syncthreads();  // rtot cleared
         atomicAdd(&rtot[rr], acc);
     }
