@@ -166,7 +166,8 @@ def copy_probe():
 def ceiling_probe(args):
     """What plain kernels reach on this GPU (libhbmprobe.so), as ceilings for
     the dispatch and combine kernels: streaming (nt) read, write and copy
-    over 1 GiB, and copies with the combine's access pattern (a 16-byte piece
+    over 1 GiB, the combine's 8:1 read/write mix on sequential streams (1 GiB
+    read, 128 MiB written, launched as the combine is), and copies with the combine's access pattern (a 16-byte piece
     of each of a token's k rows gathered into one output piece) and the FP8
     dispatch's payload pattern (a token's bf16 row stored to k rows of H
     bytes), at the prefill shape, on the canonical layout's receive rows and
@@ -188,6 +189,7 @@ def ceiling_probe(args):
     P.hbm_probe_read.argtypes = [vp, sz, vp, vp]
     P.hbm_probe_write.argtypes = [vp, sz, vp]
     P.hbm_probe_copy.argtypes = [vp, vp, sz, vp]
+    P.hbm_probe_mix8.argtypes = [vp, vp, sz, vp]
     P.hbm_probe_gather.argtypes = [vp, vp, vp, i, i, i, i, vp]
     P.hbm_probe_scatter.argtypes = [vp, vp, vp, i, i, i, i, vp]
     lib = L.lib()
@@ -233,6 +235,8 @@ def ceiling_probe(args):
         "read_1GiB": (GiB, lambda j: P.hbm_probe_read(big[j % 2].data_ptr(), GiB, sink.data_ptr(), sh)),
         "write_1GiB": (GiB, lambda j: P.hbm_probe_write(big[j % 2].data_ptr(), GiB, sh)),
         "copy_1GiB": (2 * GiB, lambda j: P.hbm_probe_copy(big[j % 2].data_ptr(), big[2 + j % 2].data_ptr(), GiB, sh)),
+        "mix8to1_1GiB": (GiB + GiB // 8, lambda j: P.hbm_probe_mix8(big[j % 2].data_ptr(), big[2 + j % 2].data_ptr(),
+                                                                    GiB // 8, sh)),
         "gather_layout_rows": (gather_b, lambda j: P.hbm_probe_gather(y[j % 2].data_ptr(), slot.data_ptr(),
                                                                       out[j % 2].data_ptr(), w.T, w.H, w.k, w.nrows, sh)),
         "gather_sequential_rows": (gather_b, lambda j: P.hbm_probe_gather(y[j % 2].data_ptr(), seq.data_ptr(),

@@ -8,6 +8,11 @@
 //    one-wave workgroups, a lane's 16-byte piece of each of the token's k
 //    rows rows[t*k + j] of y (nt loads), xor-ed, one 16-byte nt store to
 //    out[t].
+//  hbm_probe_mix8: the combine's 8:1 read/write mix with sequential
+//    streams: one-wave workgroups, as the combine launches them, each taking
+//    one 1 KB piece of each of 8 contiguous read streams and writing the xor
+//    of the eight pieces to the same place of one write stream (nt loads and
+//    stores), so every stream is read or written in ascending order.
 //  hbm_probe_scatter: the FP8 dispatch's payload pattern without the
 //    conversion: a lane reads 32 bytes of x's bf16 row t and stores 16 bytes
 //    to each of the k rows rows[t*k + j] of an H-byte-per-row buffer (nt).
@@ -101,6 +106,23 @@ __global__ __launch_bounds__(64, 8) void probe_gather_kernel(const uint16_t* __r
     }
 }
 
+__global__ __launch_bounds__(64, 8) void probe_mix8_kernel(const void* __restrict__ src, void* __restrict__ dst,
+                                                           uint32_t stream_bytes, int items) {
+    const auto rs = buffer_rsrc(src, stream_bytes * 8u);
+    const auto rd = buffer_rsrc(dst, stream_bytes);
+    for (int item = blockIdx.x; item < items; item += gridDim.x) {
+        const uint32_t off = (uint32_t)item * 1024u + threadIdx.x * 16u;
+        i32x4 v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+            v[u] = __builtin_amdgcn_raw_buffer_load_b128(rs, (int)(u * stream_bytes + off), 0, kStream);
+        i32x4 acc = v[0];
+#pragma unroll
+        for (int u = 1; u < 8; ++u) acc ^= v[u];
+        __builtin_amdgcn_raw_buffer_store_b128(acc, rd, (int)off, 0, kStream);
+    }
+}
+
 __global__ __launch_bounds__(64, 8) void probe_scatter_kernel(const uint16_t* __restrict__ x,
                                                               const int32_t* __restrict__ rows,
                                                               uint8_t* __restrict__ recv, int H, int k, int nrows,
@@ -152,6 +174,16 @@ __attribute__((visibility("default"))) int hbm_probe_copy(const void* src, void*
     if (!src || !dst || bytes == 0 || bytes >= (1ull << 31) || bytes % 16) return -1;
     hipLaunchKernelGGL(probe_copy_kernel, dim3(grid_for((uint32_t)bytes)), dim3(kThreads), 0,
                        static_cast<hipStream_t>(stream), src, dst, (uint32_t)bytes);
+    return (int)hipGetLastError();
+}
+
+// src: 8 streams of stream_bytes (a multiple of 1 KiB, 8 * stream_bytes < 2^31), dst: one stream
+__attribute__((visibility("default"))) int hbm_probe_mix8(const void* src, void* dst, size_t stream_bytes,
+                                                          void* stream) {
+    if (!src || !dst || stream_bytes == 0 || stream_bytes % 1024 || stream_bytes * 8 >= (1ull << 31)) return -1;
+    const int items = (int)(stream_bytes / 1024);
+    hipLaunchKernelGGL(probe_mix8_kernel, dim3(items < (1 << 20) ? items : (1 << 20)), dim3(64), 0,
+                       static_cast<hipStream_t>(stream), src, dst, (uint32_t)stream_bytes, items);
     return (int)hipGetLastError();
 }
 
