@@ -2,10 +2,12 @@
 the routing kernel also counts its picks per 16-token column) against the
 oracle's route and layout, bit for bit, and against the separate ep_route
 and ep_get_layout calls.  Shapes: every workload; random shapes of the
-two-tokens-per-wavefront gate (E in {128, 256, 512, 1024}, groups of whole
-32-lane slices or every group kept, m <= 2, k up to 32, any R) at token
-counts around the 16-token columns and the 64-token assign blocks, with
-normal and tie-heavy logits; and shapes that take the fallback path."""
+pair gate (E in {128, 256, 512, 1024}, groups of whole lanes or every group
+kept, m <= 2, k up to 32, any R) at token counts around the 16-token
+columns and the 64-token assign blocks, with normal and tie-heavy logits;
+the assign launch's lane strides; one and two tokens per wavefront around
+4096 tokens; and shapes that take the fallback path (among them E = 512
+and 1024, whose assign launch would need more than 64 KiB of LDS)."""
 import numpy as np
 import pytest
 import torch
@@ -134,3 +136,22 @@ def test_route_layout_zero_tokens():
     torch.cuda.synchronize()
     assert to_host(got["cnt"]).sum() == 0 and to_host(got["off"]).tolist() == [0] * (w.E + 1)
     assert to_host(got["ntok_rank"]).sum() == 0
+
+
+@pytest.mark.parametrize("E,G", [(128, 8), (128, 4), (256, 8), (256, 16)])
+def test_route_layout_column_reduction_strides(E, G):
+    # the assign launch sums each wavefront's row groups with lane strides
+    # E/16 = 8 (DPP row rotations, then row swaps) and 16 (row swaps only);
+    # E = 128 takes two tokens per wavefront in the routing launch, 256 one
+    w = W.Workload("strides", T=1000, H=128, E=E, G=G, TG=G // 2, k=8, R=32, m=2, seed=E + G)
+    assert _two_launch(w)
+    say("route_layout strides", w)
+    check(w, W.gen_logits(w))
+
+
+@pytest.mark.parametrize("T", [4095, 4096, 4097, 6000])
+def test_route_one_and_two_tokens_per_wavefront(T):
+    # the gate takes one token per wavefront up to 4096 tokens and two above
+    w = W.PREFILL.replace(name="tpw", T=T, H=128, seed=T)
+    say("route tokens per wavefront", w)
+    check(w, W.gen_logits(w), with_recv_token=T % 2 == 0)
