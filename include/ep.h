@@ -174,8 +174,10 @@ EP_API size_t ep_route_layout_workspace_bytes(const ep_config_t* cfg);
  * (the [DE] gating, then [DAY2] "DeepEP是什么" receive counts).  Arguments
  * and results are those of the two calls (logits, topk_idx and topk_w as
  * for ep_route; counts, offsets, slot and recv_token as for ep_get_layout),
- * and the results are identical.  When 32 divides E (128 <= E <= 1024),
- * m <= 2, a group covers whole 32-lane slices (or TG = G) and
+ * and the results are identical.  When the routing kernel that holds runs
+ * of consecutive experts per lane applies (32 divides E, 128 <= E <= 1024,
+ * m <= 2, a group covers whole lanes or TG = G), the assign step's scratch
+ * fits its 64 KiB of LDS (E/16 a power of two; E up to 256 at 32 ranks) and
  * 1024 < T*k with T <= 4096, the routing kernel also counts its picks per
  * block of 16 tokens into the workspace, and one more launch sums those
  * counts, scans the offsets and assigns the rows, which saves the layout's
