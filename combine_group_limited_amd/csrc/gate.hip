@@ -238,7 +238,7 @@ template <int EPL, int MC, bool HIST, int KF, int GF, int TPW>
 __global__ __launch_bounds__(kPairTokens / TPW * kWave) void gate_pair_kernel(
     const float* __restrict__ logits, int32_t* __restrict__ topk_idx, float* __restrict__ topk_w, int T, int E,
     int G_rt, int TG, int k_rt, int m, int lpg_rt, uint8_t* __restrict__ hist, uint8_t* __restrict__ rank_hist,
-    int R, int EPR, uint32_t epr_magic) {
+    int R, uint32_t epr_magic) {
     static_assert(TPW == 1 || TPW == 2, "one or two tokens per wavefront");
     constexpr int LPT = kWave / TPW;  // lanes per token
     constexpr int LPT_LOG2 = TPW == 1 ? 6 : 5;
@@ -576,10 +576,10 @@ hipError_t launch_pair_tpw(const Shape& s, int lpg_log2, const float* logits, in
     constexpr int threads = kPairTokens / TPW * kWave;
     if (hist)
         hipLaunchKernelGGL((gate_pair_kernel<EPL, MC, true, KF, GF, TPW>), dim3(blocks), dim3(threads), 0, st,
-                           logits, idx, w, s.T, s.E, s.G, s.TG, s.k, s.m, lpg_log2, hist, rank_hist, s.R, epr, magic);
+                           logits, idx, w, s.T, s.E, s.G, s.TG, s.k, s.m, lpg_log2, hist, rank_hist, s.R, magic);
     else
         hipLaunchKernelGGL((gate_pair_kernel<EPL, MC, false, KF, GF, TPW>), dim3(blocks), dim3(threads), 0, st,
-                           logits, idx, w, s.T, s.E, s.G, s.TG, s.k, s.m, lpg_log2, nullptr, nullptr, s.R, epr, magic);
+                           logits, idx, w, s.T, s.E, s.G, s.TG, s.k, s.m, lpg_log2, nullptr, nullptr, s.R, magic);
     return hipGetLastError();
 }
 
