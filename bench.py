@@ -122,15 +122,29 @@ def parse():
     return ap.parse_args()
 
 
-def buffer_sets(requested: int, touched: int, allocated: int) -> int:
-    """Copies of the buffers used round-robin: enough that >= 2 GiB of
-    touched data lies between two uses of a copy (the Infinity Cache holds
-    256 MB), at least 4, at most 256, and at most 48 GiB allocated."""
+def buffer_sets(requested: int, touched: int, allocated: int, cached: int) -> int:
+    """Copies of the buffers used round-robin, so that every step reads its
+    inputs from HBM: at least 4; enough that >= 2 GiB of touched data lies
+    between two uses of a copy; and enough that the data a step reads or
+    writes through the caches (`cached` bytes per copy: logits, x, scales and
+    the index arrays; the streaming (nt) loads and stores of the receive
+    rows, y and out do not stay in the 256 MB Infinity Cache) is at least
+    twice that cache between two uses of a copy.  Measured on MI355X at
+    prefill: with 4 copies part of x was still in the Infinity Cache (FP8
+    dispatch 56.4 us; 62.6 us with 8 or 16 copies, 49.8 us with x in the
+    cache).  At most 256 copies and 48 GiB allocated."""
     if requested:
         return requested
-    n = max(4, -(-(2 << 30) // max(touched, 1)))
+    n = max(4, -(-(2 << 30) // max(touched, 1)), 1 + -(-(512 << 20) // max(cached, 1)))
     n = min(n, 256, max(4, (48 << 30) // max(allocated, 1)))
     return int(n)
+
+
+def cached_bytes(w, scale_rows: int) -> int:
+    """Bytes per buffer copy that a step moves through the caches: logits,
+    x, the FP8 scales of `scale_rows` receive rows and the [T, k] index
+    arrays."""
+    return w.T * w.E * 4 + w.T * w.H * 2 + scale_rows * (w.H // 128) * 4 + 4 * w.T * w.k * 4
 
 
 def _copy_gbs(n: int = 1 << 30, reps: int = 5):
@@ -172,8 +186,10 @@ def ceiling_probe(args):
     dispatch's payload pattern (a token's bf16 row stored to k rows of H
     bytes), at the prefill shape, on the canonical layout's receive rows and
     on sequential rows (t*k + j), beside ep_combine and ep_dispatch on the
-    same rows.  Each probe alternates between two copies of its buffers, so
-    every run reads from HBM; HIP events around `steps` runs."""
+    same rows.  Each probe rotates over copies of its buffers, so that every
+    run reads from HBM: two of the 1 GiB buffers and of y (streamed with nt
+    loads), and 12 of x (700 MB, read through the caches: with two copies x
+    stays in the 256 MB Infinity Cache).  HIP events around `steps` runs."""
     import numpy as np
     import torch
 
@@ -208,7 +224,9 @@ def ceiling_probe(args):
     slot = lay["slot"]
     seq = torch.arange(w.nrows, dtype=torch.int32, device=dev).view(w.T, w.k)
     y = [torch.from_numpy(W.gen_y(w).view(np.int16)).view(torch.bfloat16).to(dev) for _ in range(2)]
-    x = [torch.from_numpy(W.gen_x(w).view(np.int16)).view(torch.bfloat16).to(dev) for _ in range(2)]
+    x0 = torch.from_numpy(W.gen_x(w).view(np.int16)).view(torch.bfloat16).to(dev)
+    NX = 12
+    x = [x0] + [x0.clone() for _ in range(NX - 1)]
     out = [torch.empty((w.T, w.H), dtype=torch.bfloat16, device=dev) for _ in range(2)]
     recv = [torch.empty((w.nrows, w.H), dtype=torch.uint8, device=dev) for _ in range(2)]
     sc = [torch.empty((w.nrows, w.H // 128), dtype=torch.float32, device=dev) for _ in range(2)]
@@ -245,14 +263,14 @@ def ceiling_probe(args):
         "combine_layout_rows": (w.bytes_combine(), lambda j: lib.ep_combine(cp, y[j % 2].data_ptr(), slot.data_ptr(),
                                                                            lay["w"].data_ptr(), out[j % 2].data_ptr(),
                                                                            sh)),
-        "scatter_layout_rows": (scatter_b, lambda j: P.hbm_probe_scatter(x[j % 2].data_ptr(), slot.data_ptr(),
+        "scatter_layout_rows": (scatter_b, lambda j: P.hbm_probe_scatter(x[j % NX].data_ptr(), slot.data_ptr(),
                                                                          recv[j % 2].data_ptr(), w.T, w.H, w.k,
                                                                          w.nrows, sh)),
-        "scatter_sequential_rows": (scatter_b, lambda j: P.hbm_probe_scatter(x[j % 2].data_ptr(), seq.data_ptr(),
+        "scatter_sequential_rows": (scatter_b, lambda j: P.hbm_probe_scatter(x[j % NX].data_ptr(), seq.data_ptr(),
                                                                              recv[j % 2].data_ptr(), w.T, w.H, w.k,
                                                                              w.nrows, sh)),
         "dispatch_fp8_layout_rows": (w.bytes_dispatch_fp8(),
-                                     lambda j: lib.ep_dispatch(cp, x[j % 2].data_ptr(), slot.data_ptr(),
+                                     lambda j: lib.ep_dispatch(cp, x[j % NX].data_ptr(), slot.data_ptr(),
                                                                L.EP_RECV_FP8_E4M3, recv[j % 2].data_ptr(),
                                                                sc[j % 2].data_ptr(), sh)),
     }
@@ -367,7 +385,7 @@ def run_normal(args, w):
     bytes_ = dict(route_layout=w.bytes_route() + w.bytes_layout(),
                   dispatch=w.bytes_dispatch_fp8() if fp8 else w.bytes_dispatch_bf16(), combine=w.bytes_combine())
     touched = sum(bytes_.values())
-    nsets = buffer_sets(args.sets, touched, touched)
+    nsets = buffer_sets(args.sets, touched, touched, cached_bytes(w, w.nrows if fp8 else 0))
 
     # Resident inputs and outputs, in `nsets` copies used round-robin so that
     # no step finds its data in the 256 MB Infinity Cache or the L2s.
@@ -501,7 +519,7 @@ def run_ll(args, w):
                   combine_ll=w.bytes_combine())
     touched = sum(bytes_.values())
     allocated = nrows * w.H * (1 if fp8 else 2) + nrows * w.H * 2 + touched
-    nsets = buffer_sets(args.sets, touched, allocated)
+    nsets = buffer_sets(args.sets, touched, allocated, cached_bytes(w, nrows if fp8 else 0))
 
     lg_np, x_np = W.gen_logits(w), W.gen_x(w)
     logits0 = torch.from_numpy(lg_np).to(dev)
@@ -602,7 +620,7 @@ def run_overlap(args, w):
     dev = torch.device("cuda", 0)
     ncu = torch.cuda.get_device_properties(0).multi_processor_count
     dc_bytes = w.bytes_dispatch_fp8() + w.bytes_combine()
-    nsets = buffer_sets(args.sets, dc_bytes, dc_bytes)
+    nsets = buffer_sets(args.sets, dc_bytes, dc_bytes, cached_bytes(w, w.nrows))
     lg = torch.from_numpy(W.gen_logits(w)).to(dev)
     idx, wt = ep.route(cfg, lg)
     slot = ep.get_layout(cfg, idx)["slot"]
@@ -727,7 +745,7 @@ def run_dedup(args, w):
                   partial=2 * w.H * P + 2 * w.H * rows + 16 * P,
                   combine_ranks=2 * w.H * rows + 2 * w.H * w.T + 4 * P)
     touched = sum(bytes_.values())
-    nsets = buffer_sets(args.sets, touched, touched)
+    nsets = buffer_sets(args.sets, touched, touched, cached_bytes(w, rows))
     x0 = torch.from_numpy(x_np.view(np.int16)).view(torch.bfloat16).to(dev)
     y0 = torch.from_numpy(y_np.view(np.int16)).view(torch.bfloat16).to(dev)
     i32 = dict(dtype=torch.int32, device=dev)
