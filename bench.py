@@ -10,7 +10,9 @@ are a resident synthetic buffer (the expert computation is not part of the
 path).
 
 Every buffer exists in several copies used round-robin, so that each step
-reads its inputs from HBM rather than from the 256 MB Infinity Cache.  The
+reads its inputs from HBM rather than from the 256 MB Infinity Cache
+(--warm-x shares one x between the copies instead, as when the layer before
+has just written it, and says so in `config.x`).  The
 line also reports the step replayed from a captured HIP graph that holds
 one step per buffer set (`graph_step_us`), which removes the host's launch
 gaps.
@@ -19,7 +21,8 @@ Prints one JSON line.  `value` is dispatch+combine algorithmic bytes divided
 by the summed average durations of the dispatch and combine kernels, from
 HIP events recorded on the launch stream over the timed steps.  The
 `roofline` object reports the dominant kernel (combine); `cpu_baseline`
-times the single-threaded CPU oracle on the same batch.
+times the CPU oracle on the same batch, on one thread and on every thread
+the process may use, and `parity` compares its outputs with the GPU's.
 
 Other workloads (--config), the BF16 payload (--recv-dtype bf16) and the
 low-latency path (--path ll: route + dispatch_ll + combine_ll into
@@ -28,7 +31,7 @@ dispatch+combine time in microseconds) print the same kind of line.
 
 usage: python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--config NAME]
                        [--path normal|ll] [--recv-dtype fp8|bf16]
-                       [--capacity N] [--sets N] [--no-cpu-baseline]
+                       [--capacity N] [--sets N] [--no-cpu-baseline] [--warm-x]
 """
 from __future__ import annotations
 
@@ -112,6 +115,9 @@ def parse():
     ap.add_argument("--sets", type=int, default=0,
                     help="copies of all buffers used round-robin (0: enough for >= 2 GiB between reuses)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--warm-x", action="store_true",
+                    help="normal path: every buffer set shares one x, which then stays in the Infinity Cache "
+                         "(as when the layer before has just written it); the default reads x cold")
     ap.add_argument("--cpu-seconds", type=float, default=16.0,
                     help="CPU time of the oracle legs (half on one thread, half on all threads)")
     ap.add_argument("--copy-probe", action="store_true",
@@ -399,7 +405,7 @@ def run_normal(args, w):
     for i in range(nsets):
         sets.append(dict(
             logits=logits0 if i == 0 else logits0.clone(),
-            x=x0 if i == 0 else x0.clone(),
+            x=x0 if i == 0 or args.warm_x else x0.clone(),
             y=y0 if i == 0 else y0.clone(),
             idx=torch.empty((w.T, w.k), **i32),
             wt=torch.empty((w.T, w.k), dtype=torch.float32, device=dev),
@@ -468,7 +474,8 @@ def run_normal(args, w):
         "config": {"workload": w.name, "path": "normal", "tokens": w.T, "hidden": w.H, "experts": w.E,
                    "groups": w.G, "topk_groups": w.TG, "topk": w.k, "virtual_ranks": w.R,
                    "dispatch": "fp8_e4m3_1x128_fp32_scales" if fp8 else "bf16",
-                   "combine": "bf16_fp32_accumulate", "buffer_sets": nsets},
+                   "combine": "bf16_fp32_accumulate", "buffer_sets": nsets,
+                   "x": "one copy shared by every buffer set (warm)" if args.warm_x else "own copy per buffer set"},
         "frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4),
         "dispatch_combine_us": round(dc_time * 1e6, 2),
         "tokens_per_s": round(w.T / dc_time, 1),
@@ -530,7 +537,7 @@ def run_ll(args, w):
     for i in range(nsets):
         sets.append(dict(
             logits=logits0 if i == 0 else logits0.clone(),
-            x=x0 if i == 0 else x0.clone(),
+            x=x0 if i == 0 or args.warm_x else x0.clone(),
             y=y0 if i == 0 else y0.clone(),
             idx=torch.empty((w.T, w.k), **i32),
             wt=torch.empty((w.T, w.k), dtype=torch.float32, device=dev),
