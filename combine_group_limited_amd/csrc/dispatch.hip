@@ -14,8 +14,10 @@
 // indices are loaded once per wavefront and broadcast with v_readlane.
 //
 // Cache policy, measured on MI355X at 4096 tokens x 7168 channels, top-8:
-// streaming (nt) stores of the receive rows, default-cached loads of x
-// (49.5 us; nt loads 62 us, cached stores 65 us).
+// streaming (nt) stores of the receive rows (cached stores: 65 us), and
+// default-cached loads of x.  With x still in the 256 MB Infinity Cache
+// (written or read shortly before) the cached loads take 49.5 us against
+// 62 us for nt loads; with x cold in HBM both take 62-63 us.
 #include "launch.h"
 #include "rows.h"
 

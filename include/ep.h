@@ -113,15 +113,19 @@ EP_API int ep_validate_config(const ep_config_t* cfg);
  *   topk_idx  device, int32 [T, k]  out: chosen experts, best first
  *   topk_w    device, fp32 [T, k]  out: gate weights, summing to one
  * Per token: s_e = 1 / (1 + exp(-logit_e)) in fp32, exp evaluated by Cody &
- * Waite range reduction and a degree-7 Taylor polynomial (exp(x) = +inf for
- * x > 88, 0 for x < -86); a group's score is the sum of its m best scores,
+ * Waite range reduction and a degree-7 Taylor polynomial (exp(x) = +inf from
+ * x = 88.72283935546875, the first fp32 value whose exponential exceeds
+ * FLT_MAX, and 0 below -87.33654022216797, below which it is no longer a
+ * normal number); a group's score is the sum of its m best scores,
  * largest first; the TG best groups are kept (score desc, index asc); the k
  * best experts of the kept groups are chosen (score desc, index asc); the
  * weight of pick j is s_j / ((s_0 + s_1) + ... + s_{k-1}).  Scores rank by
  * their IEEE bit pattern, which is numeric order for sigmoid's outputs.
  * Logits must not be NaN (the selection is then unspecified, still k
  * distinct in-range experts).
- * Alignment: 4 bytes.  Kernel: one 64-lane wavefront per token. */
+ * Alignment: 4 bytes.  Kernel: one 64-lane wavefront per token; above 4096
+ * tokens, for the shapes whose lanes can hold runs of consecutive experts
+ * (see ep_route_layout), one 32-lane half per token. */
 EP_API int ep_route(const ep_config_t* cfg, const float* logits,
                     int32_t* topk_idx, float* topk_w, void* stream);
 
@@ -353,9 +357,9 @@ EP_API int ep_combine_ranks(const ep_config_t* cfg, const void* partial, const i
  * and give the remaining CUs to a compute stream made the same way.  The
  * stream has the default priority.  On MI355X the HIP runtime accepts only
  * contiguous CU ranges, and a range paces the kernels by steps of 32 CUs:
- * dispatch + combine take the same time on 32 to 56 CUs and speed up again
- * at 64 (measured), so budgets that are multiples of 32, or below 32, use
- * their CUs best.  A refused stream leaves no pending HIP error behind.
+ * prefill dispatch + combine take 505-508 us on every budget from 32 to 56
+ * CUs and 297 us on 64 (measured), so budgets that are multiples of 32, or
+ * below 32, use their CUs best.  A refused stream leaves no pending HIP error behind.
  *   first_cu, num_cus  0 <= first_cu, num_cus >= 1,
  *                      first_cu + num_cus <= the device's CU count
  *   stream             host, out: the new hipStream_t
