@@ -155,3 +155,28 @@ def test_route_one_and_two_tokens_per_wavefront(T):
     w = W.PREFILL.replace(name="tpw", T=T, H=128, seed=T)
     say("route tokens per wavefront", w)
     check(w, W.gen_logits(w), with_recv_token=T % 2 == 0)
+
+
+@pytest.mark.parametrize("w", [W.DECODE, W.PREFILL.replace(T=1024), W.PREFILL.replace(T=6000)],
+                         ids=["decode", "prefill_1024", "prefill_6000"])
+def test_logits_only_four_byte_aligned(w):
+    # the routing kernel reads each lane's logits 16 bytes at a time; the ABI
+    # promises 4-byte alignment, so a row start may sit 4 bytes past a
+    # 16-byte boundary (one, two-launch and two-tokens-per-wavefront paths)
+    say("route_layout, logits at a 4-byte offset", w)
+    lg = W.gen_logits(w)
+    cfg = ep.Config.of(w)
+    buf = torch.zeros(lg.size + 1, dtype=torch.float32, device="cuda")
+    buf[1:] = to_dev(lg).view(-1)
+    d = buf[1:].view(w.T, w.E)
+    assert d.data_ptr() % 16 == 4
+    got = ep.route_layout(cfg, d)
+    idx, wt = ep.route(cfg, d)
+    torch.cuda.synchronize()
+    oi, ow = oracle.route(lg, w.G, w.TG, w.k, w.topm)
+    ol = oracle.layout(oi, w.E, w.R)
+    for name, (gi, gw) in (("route_layout", (got["idx"], got["w"])), ("route", (idx, wt))):
+        assert np.array_equal(to_host(gi), oi), name + " idx"
+        assert np.array_equal(to_host(gw).view(np.uint32), ow.view(np.uint32)), name + " w"
+    for key in KEYS:
+        assert np.array_equal(to_host(got[key]), ol[key]), key
