@@ -1,5 +1,6 @@
-"""bench.py's command line on the CPU: it refuses more than one GPU with a
-message and a non-zero status, before touching a GPU."""
+"""bench.py on the CPU: it refuses more than one GPU with a message and a
+non-zero status, before touching a GPU, and its rule for the number of
+rotating buffer copies keeps every step's inputs out of the caches."""
 import os
 import subprocess
 import sys
@@ -24,3 +25,23 @@ def test_help_lists_the_paths():
     assert r.returncode == 0
     for word in ("--path", "--config", "--steps", "--warmup", "--gpus"):
         assert word in r.stdout
+
+
+def test_buffer_copies_keep_every_step_cold():
+    # enough copies that >= 512 MB of cache-allocated data (logits, x,
+    # scales, index arrays) and >= 2 GiB of traffic lie between two uses of
+    # a copy, so no step finds its inputs in the 256 MB Infinity Cache
+    sys.path.insert(0, ROOT)
+    import bench
+    import workloads as W
+    got = {}
+    for w in (W.TINY, W.DECODE, W.PREFILL, W.LARGE):
+        touched = w.bytes_route() + w.bytes_layout() + w.bytes_dispatch_fp8() + w.bytes_combine()
+        cached = bench.cached_bytes(w, w.nrows)
+        n = bench.buffer_sets(0, touched, touched, cached)
+        got[w.name] = n
+        assert 4 <= n <= 256
+        if n < 256 and n * touched <= (48 << 30):
+            assert (n - 1) * cached >= 512 << 20 and (n - 1) * touched >= 2 << 30
+    assert got == {"tiny": 256, "decode": 244, "prefill": 9, "large": 4}
+    assert bench.buffer_sets(3, 1, 1, 1) == 3  # --sets N wins
