@@ -326,16 +326,81 @@ __global__ __launch_bounds__(TPB / TPW * kWave) void gate_pair_kernel(
         kept = rank < TG;
     }
 
+    uint32_t my_s = 0u;
+    float S = 0.0f;
+    uint64_t seen0 = 0, seen1 = 0;  // ranks picked so far, per token
+    if constexpr (TPW == 1 && EPL == 4 && KF > 0) {
+    // 3-4 with four experts per lane and one token per wavefront (256
+    // experts): each key carries its place in the lane, and the lane's keys
+    // are sorted once, so a round reads the lane's best key directly and the
+    // owner lane shifts its list.  Key = ((score bits + 1) << 2) | (3 - i):
+    // score bits are at most those of 1.0f (a NaN score, which the caller
+    // must not pass, is clamped there so that picks stay distinct), so the
+    // shift loses nothing; candidates are >= 4, non-candidates 0; within a
+    // lane equal scores put the lower expert first.  Across lanes a larger
+    // low part must not win an exact tie of scores, so a round's owner is the
+    // lowest lane whose best key has the round's best score (key >= that
+    // score's lowest key).
+    constexpr uint32_t kOneBits = 0x3F800000u;
+    uint32_t q[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        q[i] = (kept && live) ? (((min(sb[i], kOneBits) + 1u) << 2) | (uint32_t)(3 - i)) : 0u;
+    {
+        auto cx = [](uint32_t& a, uint32_t& b) {  // a >= b afterwards
+            const uint32_t hi = max(a, b), lo = min(a, b);
+            a = hi;
+            b = lo;
+        };
+        cx(q[0], q[1]);
+        cx(q[2], q[3]);
+        cx(q[0], q[2]);
+        cx(q[1], q[3]);
+        cx(q[1], q[2]);
+    }
+    uint32_t pe[KF > 0 ? KF : 1], ps[KF > 0 ? KF : 1];
+    for_count<KF>(k, [&](int j) {
+        uint32_t v = q[0];
+        v = max(v, dpp_u32<kDppXor1>(v));
+        v = max(v, dpp_u32<kDppXor2>(v));
+        v = max(v, dpp_u32<kDppHalfMirror>(v));
+        v = max(v, dpp_u32<kDppMirror>(v));
+        v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, kDppRowBcast15, 0xA, 0xF, false));
+        v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, kDppRowBcast31, 0xC, 0xF, false));
+        const uint32_t tgt = (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+        const uint64_t eq = __ballot(q[0] >= (tgt & ~3u));
+        const int o0 = __ffsll((unsigned long long)eq) - 1;
+        const uint32_t hb = (uint32_t)__builtin_amdgcn_readlane((int)q[0], o0);
+        const bool owner = lane == o0;
+        q[0] = owner ? q[1] : q[0];
+        q[1] = owner ? q[2] : q[1];
+        q[2] = owner ? q[3] : q[2];
+        q[3] = owner ? 0u : q[3];
+        const uint32_t e = (uint32_t)o0 * 4u + (3u - (hb & 3u));
+        const uint32_t sbits = (tgt >> 2) - 1u;
+        pe[j] = e;
+        ps[j] = sbits;
+        S = S + __uint_as_float(sbits);
+        if (HIST) {
+            const uint32_t r0 = rank_of(e, epr_magic) & 63u;
+            first0 |= (uint64_t)(((seen0 >> r0) & 1ull) ^ 1ull) << j;
+            seen0 |= 1ull << r0;
+        }
+    });
+    // pick j to lane j (the picks are wave-uniform), after the rounds
+    for_count<KF>(k, [&](int j) {
+        const bool mine = hl == j;
+        my_e = mine ? (int)pe[j] : my_e;
+        my_s = mine ? ps[j] : my_s;
+    });
+    } else {
     // 3. candidate keys (non-candidates, and a half with no token, hold 0)
     uint32_t key[EPL];
 #pragma unroll
     for (int i = 0; i < EPL; ++i) key[i] = (kept && live) ? (sb[i] | kCandidate) : 0u;
 
     // 4. k rounds
-    uint32_t my_s = 0u;
-    float S = 0.0f;
     const uint32_t hsel = half ? ~0u : 0u;  // selects the upper half's value of a pair
-    uint64_t seen0 = 0, seen1 = 0;          // ranks picked so far, per token
     for_count<KF>(k, [&](int j) {
         uint32_t bk = key[0];
 #pragma unroll
@@ -399,6 +464,7 @@ __global__ __launch_bounds__(TPB / TPW * kWave) void gate_pair_kernel(
             }
         }
     });
+    }
 
     // 5. weights
     if (live && hl < k) {
