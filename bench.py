@@ -113,7 +113,8 @@ def parse():
     ap.add_argument("--recv-dtype", choices=("fp8", "bf16"), default="fp8", help="dispatch payload")
     ap.add_argument("--capacity", type=int, default=0, help="low-latency rows per expert (0: T)")
     ap.add_argument("--sets", type=int, default=0,
-                    help="copies of all buffers used round-robin (0: enough for >= 2 GiB between reuses)")
+                    help="copies of all buffers used round-robin (0: enough that every step reads its inputs "
+                         "from HBM, not from the caches)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--warm-x", action="store_true",
                     help="normal path: every buffer set shares one x, which then stays in the Infinity Cache "
@@ -839,6 +840,9 @@ def main():
     if args.gpus != 1:
         print("bench.py measures one GPU only: the library has no multi-GPU exchange "
               "(--gpus %d requested)" % args.gpus, file=sys.stderr)
+        return 2
+    if args.warm_x and args.path != "normal":
+        print("--warm-x applies to the normal path only (--path %s requested)" % args.path, file=sys.stderr)
         return 2
     if args.copy_probe:
         return copy_probe()

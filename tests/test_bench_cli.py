@@ -20,6 +20,12 @@ def test_more_than_one_gpu_is_refused():
     assert r.stdout == ""
 
 
+def test_warm_x_is_refused_outside_the_normal_path():
+    r = run("--path", "ll", "--warm-x")
+    assert r.returncode != 0
+    assert "--warm-x" in r.stderr and r.stdout == ""
+
+
 def test_help_lists_the_paths():
     r = run("--help")
     assert r.returncode == 0
