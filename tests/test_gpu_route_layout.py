@@ -7,7 +7,10 @@ kept, m <= 2, k up to 32, any R) at token counts around the 16-token
 columns and the 64-token assign blocks, with normal and tie-heavy logits;
 the assign launch's lane strides; one and two tokens per wavefront around
 4096 tokens; and shapes that take the fallback path (among them E = 512
-and 1024, whose assign launch would need more than 64 KiB of LDS)."""
+and 1024, whose assign launch would need more than 64 KiB of LDS); exact score
+ties for the pick rounds of 256 experts, four per lane; logits only 4-byte
+aligned; and NaN logits (outside the contract: k distinct experts in range
+per token, the other tokens as the oracle routes them)."""
 import numpy as np
 import pytest
 import torch
@@ -180,3 +183,54 @@ def test_logits_only_four_byte_aligned(w):
         assert np.array_equal(to_host(gw).view(np.uint32), ow.view(np.uint32)), name + " w"
     for key in KEYS:
         assert np.array_equal(to_host(got[key]), ol[key]), key
+
+
+@pytest.mark.parametrize("case", range(8))
+def test_sorted_key_rounds_with_exact_ties(case):
+    # 256 experts in 8 groups, top-8, one token per wavefront: the pick rounds
+    # read each lane's sorted keys, whose low bits hold the expert's place in
+    # the lane; exact score ties within a lane and across lanes must still go
+    # to the lower expert index.  Logits from one to four distinct values
+    # (exactly equal, or 1-2 ulps apart), group limit on and off, with and
+    # without the pick counts.
+    rng = np.random.default_rng(9100 + case)
+    TG = 8 if case % 4 == 0 else 4
+    T = (77, 1000, 3000, 4096)[case % 4]
+    w = W.PREFILL.replace(name="ties256", T=T, H=128, TG=TG, m=1 if TG == 8 else 2, seed=9100 + case)
+    vals = np.float32([-1.5, 0.0, 0.25, 3.0])
+    lg = rng.choice(vals[: 1 + case % 4], size=(w.T, w.E)).astype(np.float32)
+    if case % 2:
+        steps = rng.integers(0, 3, size=(w.T, w.E)).astype(np.int32)
+        lg = (lg.view(np.int32) + np.where(lg >= 0, steps, -steps)).view(np.float32)
+    say("sorted-key rounds, ties", case, w)
+    check(w, lg, with_recv_token=bool(case % 2))
+
+
+@pytest.mark.parametrize("w", [
+    W.PREFILL.replace(name="nan256", T=1000, H=128, seed=71),                       # sorted-key rounds
+    W.DECODE.replace(name="nan_decode", H=128, seed=72),                            # every group kept
+    W.Workload("nan128", T=600, H=128, E=128, G=8, TG=4, k=8, R=16, seed=73),       # lanes of 4, G=8
+    W.Workload("nan_e96", T=300, H=128, E=96, G=4, TG=2, k=6, R=12, m=3, seed=74),  # general gate
+], ids=["e256", "decode", "e128", "e96"])
+def test_nan_logits_still_give_distinct_picks(w):
+    # NaN logits are outside the contract (the selection is unspecified), but
+    # every token must still get k distinct experts in range, and tokens
+    # without a NaN are routed exactly as the oracle routes them
+    rng = np.random.default_rng(w.seed)
+    lg = W.gen_logits(w)
+    bad = rng.random(w.T) < 0.3
+    for t in np.flatnonzero(bad):
+        lg[t, rng.choice(w.E, size=int(rng.integers(1, w.E + 1)), replace=False)] = np.nan
+    say("NaN logits", w, int(bad.sum()), "tokens with NaN")
+    cfg = ep.Config.of(w)
+    d = to_dev(lg)
+    got = ep.route_layout(cfg, d)
+    idx, _ = ep.route(cfg, d)
+    torch.cuda.synchronize()
+    ok = ~bad
+    oi, ow = oracle.route(np.ascontiguousarray(lg[ok]), w.G, w.TG, w.k, w.topm)
+    for name, gi in (("route_layout", to_host(got["idx"])), ("route", to_host(idx))):
+        assert ((gi >= 0) & (gi < w.E)).all(), name
+        assert all(len(set(row)) == w.k for row in gi.tolist()), name + ": repeated expert"
+        assert np.array_equal(gi[ok], oi), name + ": tokens without NaN"
+    assert np.array_equal(to_host(got["w"])[ok].view(np.uint32), ow.view(np.uint32))
