@@ -30,10 +30,13 @@
 // Measured on MI355X, 256 experts in 8 groups, top-4 groups, top-8, back to
 // back with the pick counts (HIP events): 128 tokens 5.3 us, 4096 tokens
 // 5.7 us with one token per wavefront (6.5 us with two; gate_fast_kernel
-// 8.9 us); 16384 tokens 14.5 us with two (18.9 us with one).  One wave's
+// 8.9 us); 16384 tokens 14.5 us with two (18.9 us with one).  Without the
+// counts, in 4-token workgroups, 128 tokens take 3.5 us.  One wave's
 // dependency chain sets the time up to a few thousand tokens: the first
-// load of its logits from HBM (~1.8 us), the k pick rounds (~700 cycles
-// each) and the workgroup barrier before the counts are written.
+// load of its logits from HBM (~1.8 us), the k pick rounds (DPP steps with
+// their wait states, lane reads, ballot) and, with counts, the workgroup
+// barrier before they are written; at 4096 tokens four wavefronts share
+// each SIMD and keep its VALU about half busy.
 #include "device.h"
 #include "launch.h"
 
