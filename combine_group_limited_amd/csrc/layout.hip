@@ -428,7 +428,8 @@ constexpr int kRankBatch = 16;
 //     before the block (its rows before the block).  A 16-byte load holds
 //     sixteen experts' counts of one column; thread (g, d) reads piece d of
 //     the rows g, g + RG, ... (TPR = E/16 threads per row, RG = NT / TPR row
-//     groups), kColBatch loads at a time, adds them as packed bytes and
+//     groups), kColBatch loads at a time through one buffer resource over
+//     the columns (rows past the last read zeros), adds them as packed bytes and
 //     unpacks each batch into 16-bit pairs (a column count is at most
 //     CT = 16, so a batch's sum fits a byte; a sum of all C <= 256 columns
 //     fits 16 bits).  The row groups inside a wavefront meet by lane
@@ -476,24 +477,28 @@ __global__ __launch_bounds__(W * 64) void layout_assign_cols_kernel(
         const int TPR = E >> 4;     // threads per row (a power of two <= 64)
         const int RG = NT / TPR;    // row groups
         const int d = tid & (TPR - 1), g = tid / TPR;
-        const u32x4* h = reinterpret_cast<const u32x4*>(hist) + d;
+        // unconditional loads through one resource over the C columns (the
+        // workspace, global memory): a row past the last reads zeros, so
+        // only the rows before the block need a mask
+        const auto hr = buffer_rsrc(hist, (uint32_t)C * (uint32_t)E);
         uint32_t pp[8], pa[8];  // 16-bit count pairs: word 2q + h holds experts 4q + 2h (low), 4q + 2h + 1
 #pragma unroll
         for (int i = 0; i < 8; ++i) pp[i] = pa[i] = 0u;
         for (int r0 = g; r0 < C; r0 += kColBatch * RG) {
-            // unconditional loads (row clamped into [0, C), its value masked)
             u32x4 v[kColBatch];
+            const uint32_t o0 = (uint32_t)r0 * (uint32_t)E + 16u * (uint32_t)d;
 #pragma unroll
             for (int u = 0; u < kColBatch; ++u) {
-                const int r = r0 + u * RG;
-                v[u] = h[(size_t)(r < C ? r : C - 1) * TPR];
+                const i32x4 t = __builtin_amdgcn_raw_buffer_load_b128(hr, (int)(o0 + (uint32_t)(u * RG * E)), 0,
+                                                                      kCached);
+                v[u] = u32x4{(uint32_t)t.x, (uint32_t)t.y, (uint32_t)t.z, (uint32_t)t.w};
             }
             u32x4 bp = u32x4{0, 0, 0, 0}, ba = u32x4{0, 0, 0, 0};  // packed byte sums of the batch
 #pragma unroll
             for (int u = 0; u < kColBatch; ++u) {
                 const int r = r0 + u * RG;
                 const u32x4 z = u32x4{0, 0, 0, 0};
-                ba += r < C ? v[u] : z;
+                ba += v[u];
                 bp += r < c0 ? v[u] : z;  // c0 <= C
             }
 #pragma unroll
