@@ -74,7 +74,6 @@ def _ptr(t) -> int:
     return 0 if t is None else t.data_ptr()
 
 
-
 def _want(t: torch.Tensor, name: str, shape, dtype, device) -> None:
     if not isinstance(t, torch.Tensor):
         raise TypeError("%s must be a torch.Tensor" % name)
