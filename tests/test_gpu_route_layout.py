@@ -1,16 +1,17 @@
-"""ep_route_layout (routing followed by the layout, in two launches where
-the routing kernel also counts its picks per 16-token column) against the
+"""ep_route_layout (routing followed by the layout, in two launches where the
+routing kernel also counts its picks per 16-token column) against the
 oracle's route and layout, bit for bit, and against the separate ep_route
-and ep_get_layout calls.  Shapes: every workload; random shapes of the
-pair gate (E in {128, 256, 512, 1024}, groups of whole lanes or every group
-kept, m <= 2, k up to 32, any R) at token counts around the 16-token
-columns and the 64-token assign blocks, with normal and tie-heavy logits;
-the assign launch's lane strides; one and two tokens per wavefront around
-4096 tokens; and shapes that take the fallback path (among them E = 512
-and 1024, whose assign launch would need more than 64 KiB of LDS); exact score
-ties for the pick rounds of 256 experts, four per lane; logits only 4-byte
-aligned; and NaN logits (outside the contract: k distinct experts in range
-per token, the other tokens as the oracle routes them)."""
+and ep_get_layout calls. Shapes: every workload; random shapes of the pair
+gate (E in {128, 256, 512, 1024}, groups of whole lanes or every group kept,
+m <= 2, k up to 32, any R) at token counts around the 16-token columns and
+the 64-token assign blocks, with normal and tie-heavy logits; the assign
+launch's lane strides; one and two tokens per wavefront around 4096 tokens
+(top-6 keeps the switch, top-8 of 8 groups stays at one); and shapes that
+take the fallback path (among them E = 512 and 1024, whose assign launch
+would need more than 64 KiB of LDS); exact score ties for the pick rounds of
+256 experts, four per lane; logits only 4-byte aligned; and NaN logits
+(outside the contract: k distinct experts in range per token, the other
+tokens as the oracle routes them)."""
 import numpy as np
 import pytest
 import torch
@@ -152,10 +153,12 @@ def test_route_layout_column_reduction_strides(E, G):
     check(w, W.gen_logits(w))
 
 
-@pytest.mark.parametrize("T", [4095, 4096, 4097, 6000])
-def test_route_one_and_two_tokens_per_wavefront(T):
-    # the gate takes one token per wavefront up to 4096 tokens and two above
-    w = W.PREFILL.replace(name="tpw", T=T, H=128, seed=T)
+@pytest.mark.parametrize("T,k", [(4095, 8), (4096, 8), (4097, 8), (6000, 8), (4096, 6), (4097, 6), (6000, 6)])
+def test_route_one_and_two_tokens_per_wavefront(T, k):
+    # the gate takes one token per wavefront up to 4096 tokens and two above,
+    # except for the sorted-key rounds (256 experts, top-8 of 8 groups),
+    # which keep one token per wavefront at every size
+    w = W.PREFILL.replace(name="tpw", T=T, H=128, k=k, seed=T + k)
     say("route tokens per wavefront", w)
     check(w, W.gen_logits(w), with_recv_token=T % 2 == 0)
 
