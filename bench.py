@@ -500,7 +500,8 @@ def run_normal(args, w):
             return t.view(torch.int16).numpy().view(np.uint16) if t.dtype == torch.bfloat16 else t.numpy()
 
         gpu = {k: to_host(v) for k, v in sets[0].items()
-               if k in ("idx", "wt", "cnt", "ntok", "off", "slot", "recv_token", "recv", "scales", "out")}
+               if v is not None and k in ("idx", "wt", "cnt", "ntok", "off", "slot", "recv_token", "recv",
+                                          "scales", "out")}
         rec["parity"], _, wt_o, lay_o = oracle_parity(w, fp8, gpu, lg_np, x_np, y_np)
         del gpu
         rec["cpu_baseline"] = cpu_baseline(w, fp8, x_np, y_np, wt_o, lay_o, args.cpu_seconds)
