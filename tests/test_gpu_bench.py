@@ -56,9 +56,19 @@ def test_normal_path_record(recv_dtype):
     assert rec["config"]["buffer_sets"] == 2 and rec["config"]["workload"] == "tiny"
 
 
-def test_low_latency_record():
-    say("bench low-latency path, tiny")
-    rec = bench.run_ll(args_for("--path", "ll", "--steps", "2", "--warmup", "1", "--sets", "2"), W.TINY)
+def test_normal_path_with_warm_x():
+    say("bench normal path, tiny, x shared between the buffer sets")
+    a = args_for("--steps", "2", "--warmup", "1", "--sets", "3", "--warm-x", "--no-cpu-baseline")
+    rec = bench.run_normal(a, W.TINY)
+    check_line(rec, 2)
+    assert rec["config"]["x"].startswith("one copy shared")
+
+
+@pytest.mark.parametrize("recv_dtype", ["fp8", "bf16"])
+def test_low_latency_record(recv_dtype):
+    say("bench low-latency path, tiny,", recv_dtype)
+    a = args_for("--path", "ll", "--steps", "2", "--warmup", "1", "--sets", "2", "--recv-dtype", recv_dtype)
+    rec = bench.run_ll(a, W.TINY)
     check_line(rec, 2)
     assert rec["higher_is_better"] is False and rec["unit"].startswith("us")
 
