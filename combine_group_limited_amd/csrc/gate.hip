@@ -332,17 +332,18 @@ __global__ __launch_bounds__(TPB / TPW * kWave) void gate_pair_kernel(
     uint32_t my_s = 0u;
     float S = 0.0f;
     uint64_t seen0 = 0, seen1 = 0;  // ranks picked so far, per token
-    if constexpr (TPW == 1 && EPL == 4 && KF > 0) {
-    // 3-4 with four experts per lane and one token per wavefront (256
-    // experts): each key carries its place in the lane, and the lane's keys
-    // are sorted once, so a round reads the lane's best key directly and the
-    // owner lane shifts its list.  Key = ((score bits + 1) << 2) | (3 - i):
-    // score bits are at most those of 1.0f (a NaN score, which the caller
-    // must not pass, is clamped there so that picks stay distinct), so the
-    // shift loses nothing; candidates are >= 4, non-candidates 0; within a
-    // lane equal scores put the lower expert first.  Across lanes a larger
-    // low part must not win an exact tie of scores, so a round's owner is the
-    // lowest lane whose best key has the round's best score (key >= that
+    if constexpr (EPL == 4) {
+    // 3-4 with four experts per lane (256 experts at one token per
+    // wavefront, 128 at two): each key carries its place in the lane, and the
+    // lane's keys are sorted once, so a round reads the lane's best key
+    // directly and the owner lane shifts its list.  Key = ((score bits + 1)
+    // << 2) | (3 - i): score bits are at most those of 1.0f (a NaN score,
+    // which the caller must not pass, is clamped there so that picks stay
+    // distinct), so the shift loses nothing; candidates are >= 4,
+    // non-candidates and a half with no token 0; within a lane equal scores
+    // put the lower expert first.  Across lanes a larger low part must not
+    // win an exact tie of scores, so a round's owner is the lowest lane of
+    // the token whose best key has the round's best score (key >= that
     // score's lowest key).
     constexpr uint32_t kOneBits = 0x3F800000u;
     uint32_t q[4];
@@ -361,41 +362,79 @@ __global__ __launch_bounds__(TPB / TPW * kWave) void gate_pair_kernel(
         cx(q[1], q[3]);
         cx(q[1], q[2]);
     }
-    uint32_t pe[KF > 0 ? KF : 1], ps[KF > 0 ? KF : 1];
+    const uint32_t hsel = half ? ~0u : 0u;  // selects the upper half's value of a pair
+    uint32_t pe0[KF > 0 ? KF : 1], ps0[KF > 0 ? KF : 1], pe1[KF > 0 ? KF : 1], ps1[KF > 0 ? KF : 1];
     for_count<KF>(k, [&](int j) {
+        // each token's best key: row butterflies, then rows 0 -> 1 and
+        // 2 -> 3 (and 1 -> 2, 3 for one token per wavefront)
         uint32_t v = q[0];
         v = max(v, dpp_u32<kDppXor1>(v));
         v = max(v, dpp_u32<kDppXor2>(v));
         v = max(v, dpp_u32<kDppHalfMirror>(v));
         v = max(v, dpp_u32<kDppMirror>(v));
         v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, kDppRowBcast15, 0xA, 0xF, false));
-        v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, kDppRowBcast31, 0xC, 0xF, false));
-        const uint32_t tgt = (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
-        const uint64_t eq = __ballot(q[0] >= (tgt & ~3u));
-        const int o0 = __ffsll((unsigned long long)eq) - 1;
-        const uint32_t hb = (uint32_t)__builtin_amdgcn_readlane((int)q[0], o0);
-        const bool owner = lane == o0;
+        uint32_t m0, m1 = 0u, hb1 = 0u;
+        int o0, o1 = 32;
+        uint64_t eq;
+        if constexpr (TPW == 2) {
+            m0 = (uint32_t)__builtin_amdgcn_readlane((int)v, 31);
+            m1 = (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+            const uint32_t tgt = m0 ^ ((m0 ^ m1) & hsel);
+            eq = __ballot(q[0] >= (tgt & ~3u));
+            o0 = __ffsll((unsigned long long)(eq & ~kHiHalf)) - 1;
+            o1 = __ffsll((unsigned long long)(eq & kHiHalf)) - 1;
+            hb1 = (uint32_t)__builtin_amdgcn_readlane((int)q[0], o1);
+        } else {
+            v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, kDppRowBcast31, 0xC, 0xF, false));
+            m0 = (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+            eq = __ballot(q[0] >= (m0 & ~3u));
+            o0 = __ffsll((unsigned long long)eq) - 1;
+        }
+        const uint32_t hb0 = (uint32_t)__builtin_amdgcn_readlane((int)q[0], o0);
+        const bool owner = lane == o0 || (TPW == 2 && lane == o1);
         q[0] = owner ? q[1] : q[0];
         q[1] = owner ? q[2] : q[1];
         q[2] = owner ? q[3] : q[2];
         q[3] = owner ? 0u : q[3];
-        const uint32_t e = (uint32_t)o0 * 4u + (3u - (hb & 3u));
-        const uint32_t sbits = (tgt >> 2) - 1u;
-        pe[j] = e;
-        ps[j] = sbits;
-        S = S + __uint_as_float(sbits);
+        // the picks (wave-uniform): expert and score bits of each token
+        const uint32_t e0 = (uint32_t)o0 * 4u + (3u - (hb0 & 3u));
+        const uint32_t s0 = (m0 >> 2) - 1u;
+        const uint32_t e1 = (uint32_t)(o1 - 32) * 4u + (3u - (hb1 & 3u));
+        const uint32_t s1 = (m1 >> 2) - 1u;
+        const uint32_t sm = TPW == 2 ? (s0 ^ ((s0 ^ s1) & hsel)) : s0;
+        S = S + __uint_as_float(sm);
+        if constexpr (KF > 0) {
+            pe0[j] = e0;
+            ps0[j] = s0;
+            pe1[j] = e1;
+            ps1[j] = s1;
+        } else {
+            const bool mine = hl == j;
+            const uint32_t em = TPW == 2 ? (e0 ^ ((e0 ^ e1) & hsel)) : e0;
+            my_e = mine ? (int)em : my_e;
+            my_s = mine ? sm : my_s;
+        }
         if (HIST) {
-            const uint32_t r0 = rank_of(e, epr_magic) & 63u;
+            const uint32_t r0 = rank_of(e0, epr_magic) & 63u;
             first0 |= (uint64_t)(((seen0 >> r0) & 1ull) ^ 1ull) << j;
             seen0 |= 1ull << r0;
+            if (TPW == 2) {
+                const uint32_t r1 = rank_of(e1, epr_magic) & 63u;
+                first1 |= (uint64_t)(((seen1 >> r1) & 1ull) ^ 1ull) << j;
+                seen1 |= 1ull << r1;
+            }
         }
     });
-    // pick j to lane j (the picks are wave-uniform), after the rounds
-    for_count<KF>(k, [&](int j) {
-        const bool mine = hl == j;
-        my_e = mine ? (int)pe[j] : my_e;
-        my_s = mine ? ps[j] : my_s;
-    });
+    if constexpr (KF > 0) {
+        // pick j to lane j of its token, after the rounds
+        for_count<KF>(k, [&](int j) {
+            const bool mine = hl == j;
+            const uint32_t em = TPW == 2 ? (pe0[j] ^ ((pe0[j] ^ pe1[j]) & hsel)) : pe0[j];
+            const uint32_t sm = TPW == 2 ? (ps0[j] ^ ((ps0[j] ^ ps1[j]) & hsel)) : ps0[j];
+            my_e = mine ? (int)em : my_e;
+            my_s = mine ? sm : my_s;
+        });
+    }
     } else {
     // 3. candidate keys (non-candidates, and a half with no token, hold 0)
     uint32_t key[EPL];

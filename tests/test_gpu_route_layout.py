@@ -188,18 +188,22 @@ def test_logits_only_four_byte_aligned(w):
         assert np.array_equal(to_host(got[key]), ol[key]), key
 
 
-@pytest.mark.parametrize("case", range(8))
+@pytest.mark.parametrize("case", range(16))
 def test_sorted_key_rounds_with_exact_ties(case):
-    # 256 experts in 8 groups, top-8, one token per wavefront: the pick rounds
-    # read each lane's sorted keys, whose low bits hold the expert's place in
-    # the lane; exact score ties within a lane and across lanes must still go
-    # to the lower expert index.  Logits from one to four distinct values
-    # (exactly equal, or 1-2 ulps apart), group limit on and off, with and
-    # without the pick counts.
+    # four experts per lane (256 experts at one token per wavefront, 128 at
+    # two): the pick rounds read each lane's sorted keys, whose low bits hold
+    # the expert's place in the lane; exact score ties within a lane and
+    # across lanes must still go to the lower expert index.  Logits from one
+    # to four distinct values (exactly equal, or 1-2 ulps apart), group limit
+    # on and off, with and without the pick counts; top-8 of 8 groups (picks
+    # unrolled) and top-6 or 16 groups (picks counted at run time).
     rng = np.random.default_rng(9100 + case)
-    TG = 8 if case % 4 == 0 else 4
+    E = 256 if case < 8 or case % 2 else 128
+    G, k = (8, 8) if case < 12 else (16, 6)
+    TG = G if case % 4 == 0 else G // 2
     T = (77, 1000, 3000, 4096)[case % 4]
-    w = W.PREFILL.replace(name="ties256", T=T, H=128, TG=TG, m=1 if TG == 8 else 2, seed=9100 + case)
+    w = W.PREFILL.replace(name="ties%d" % E, T=T, H=128, E=E, G=G, TG=TG, k=k, R=16,
+                          m=1 if TG == G else 2, seed=9100 + case)
     vals = np.float32([-1.5, 0.0, 0.25, 3.0])
     lg = rng.choice(vals[: 1 + case % 4], size=(w.T, w.E)).astype(np.float32)
     if case % 2:
