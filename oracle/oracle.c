@@ -40,7 +40,10 @@ static float u2f(uint32_t u) { float f; memcpy(&f, &u, 4); return f; }
 static int   g_consts_ready = 0;
 static float g_l2e, g_c1, g_c2, g_p[8], g_hi, g_lo;
 
-static void exp_consts(void) {
+/* Runs when the library is loaded (before any caller's thread can reach
+ * orc_expf), so the constants are never written while another thread reads
+ * them; the calls below then only see g_consts_ready set. */
+__attribute__((constructor)) static void exp_consts(void) {
     if (g_consts_ready) return;
     double ln2 = log(2.0);
     g_l2e = (float)(1.0 / ln2);
