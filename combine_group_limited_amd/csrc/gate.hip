@@ -9,9 +9,9 @@
 //
 // Three kernels compute the same result:
 //  - gate_pair_kernel, one or two tokens per wavefront (the token's 64 or 32
-//    lanes each holding a run of consecutive experts), when the lanes divide
-//    E (128 <= E <= 1024), m <= 2 and a group is a power-of-two run of whole
-//    lanes (or TG = G).  Group scores are mostly in-lane, and with two
+//    lanes each holding a run of 4, 8, 16 or 32 consecutive experts: E =
+//    128, 256, 512 or 1024), when m <= 2 and a group is a power-of-two run
+//    of whole lanes (or TG = G).  Group scores are mostly in-lane, and with two
 //    tokens each cross-lane step serves both.  It can also count its picks
 //    per workgroup for the routing layout (HIST).
 //  - gate_fast_kernel, one wavefront per token, lane l holding experts l,
@@ -729,14 +729,16 @@ hipError_t launch_pair_mc(const Shape& s, int tpw, int mc, int lpg_log2, const f
 }
 
 // The pair kernel applies with `tpw` tokens per wavefront (LPT = 64 / tpw
-// lanes per token): LPT | E with 4 <= E/LPT <= 32 (E/LPT experts per lane,
-// read 16 bytes at a time), E <= 1024, m <= 2, and either every group is kept
-// or a group is a power-of-two run of whole lanes of the token's lanes.
+// lanes per token): E/LPT experts per lane, a power of two from 4 to 32 (the
+// kernel's instances, read 16 bytes at a time), E <= 1024, m <= 2, and
+// either every group is kept or a group is a power-of-two run of whole lanes
+// of the token's lanes.
 bool pair_gate_shape(const Shape& s, int tpw, int* epl, int* lpg_log2, int* mc) {
     const int LPT = kWave / tpw;
     if (s.E % LPT != 0 || s.E < 4 * LPT || s.E > 32 * LPT || s.E > 1024 || s.m > 2) return false;
     const int GS = s.E / s.G;
     *epl = s.E / LPT;
+    if ((*epl & (*epl - 1)) != 0) return false;  // 4, 8, 16 or 32 experts per lane
     *lpg_log2 = 0;
     while ((*epl << *lpg_log2) < GS) ++*lpg_log2;
     const bool lanes_ok = GS % *epl == 0 && (*epl << *lpg_log2) == GS && (1 << *lpg_log2) <= LPT;
@@ -762,7 +764,8 @@ hipError_t launch_pair_any(const Shape& s, int tpw, int epl, int lpg_log2, int m
     if (epl == 4) return launch_pair_mc<4>(s, tpw, mc, lpg_log2, logits, idx, w, hist, rank_hist, st);
     if (epl == 8) return launch_pair_mc<8>(s, tpw, mc, lpg_log2, logits, idx, w, hist, rank_hist, st);
     if (epl == 16) return launch_pair_mc<16>(s, tpw, mc, lpg_log2, logits, idx, w, hist, rank_hist, st);
-    return launch_pair_mc<32>(s, tpw, mc, lpg_log2, logits, idx, w, hist, rank_hist, st);
+    if (epl == 32) return launch_pair_mc<32>(s, tpw, mc, lpg_log2, logits, idx, w, hist, rank_hist, st);
+    return hipErrorInvalidValue;  // pair_gate_shape admits no other count
 }
 
 template <int EPL>

@@ -179,7 +179,7 @@ EP_API size_t ep_route_layout_workspace_bytes(const ep_config_t* cfg);
  * and results are those of the two calls (logits, topk_idx and topk_w as
  * for ep_route; counts, offsets, slot and recv_token as for ep_get_layout),
  * and the results are identical.  When the routing kernel that holds runs
- * of consecutive experts per lane applies (32 divides E, 128 <= E <= 1024,
+ * of consecutive experts per lane applies (E = 128, 256, 512 or 1024,
  * m <= 2, a group covers whole lanes or TG = G), the assign step's scratch
  * fits its 64 KiB of LDS (E/16 a power of two; E up to 256 at 32 ranks) and
  * 1024 < T*k with T <= 4096, the routing kernel also counts its picks per

@@ -8,10 +8,11 @@ the 64-token assign blocks, with normal and tie-heavy logits; the assign
 launch's lane strides; one and two tokens per wavefront around 4096 tokens
 (top-6 keeps the switch, top-8 of 8 groups stays at one); and shapes that
 take the fallback path (among them E = 512 and 1024, whose assign launch
-would need more than 64 KiB of LDS); exact score ties for the pick rounds of
-256 experts, four per lane; logits only 4-byte aligned; and NaN logits
-(outside the contract: k distinct experts in range per token, the other
-tokens as the oracle routes them)."""
+would need more than 64 KiB of LDS, and E with a count of experts per
+lane that is not a power of two: 160, 192, 320, 384, 640 and 768); exact
+score ties for the pick rounds of 256 experts, four per lane; logits only
+4-byte aligned; and NaN logits (outside the contract: k distinct experts
+in range per token, the other tokens as the oracle routes them)."""
 import numpy as np
 import pytest
 import torch
@@ -131,6 +132,22 @@ def test_route_layout_column_and_block_edges(T, k):
 def test_route_layout_fallback_shapes(w):
     say("route_layout fallback", w)
     check(w, W.gen_logits(w))
+
+
+@pytest.mark.parametrize("w", [
+    W.Workload("epl6", T=700, H=128, E=384, G=16, TG=8, k=8, R=48, m=2, seed=51),      # 6 per lane
+    W.Workload("epl5", T=500, H=128, E=320, G=64, TG=16, k=8, R=40, m=2, seed=52),     # 5 per lane
+    W.Workload("epl10", T=300, H=128, E=640, G=64, TG=8, k=8, R=64, m=2, seed=53),     # 10 per lane
+    W.Workload("epl12", T=200, H=128, E=768, G=8, TG=8, k=8, R=96, m=1, seed=54),      # 12, all groups
+    W.Workload("epl6h", T=5000, H=128, E=192, G=8, TG=4, k=6, R=24, m=2, seed=55),     # 6 per half-wave lane
+    W.Workload("epl5h", T=4500, H=128, E=160, G=5, TG=5, k=6, R=20, m=0, seed=56),     # 5, all groups
+], ids=lambda w: w.name)
+def test_route_layout_experts_per_lane_not_a_power_of_two(w):
+    # E a multiple of the token's lanes, but E / lanes not 4, 8, 16 or 32:
+    # the routing kernel that holds runs of experts per lane has no such
+    # instance, so these shapes take the other gate kernels
+    say("route_layout experts per lane", w)
+    check(w, W.gen_logits(w), with_recv_token=w.T % 2 == 0)
 
 
 def test_route_layout_zero_tokens():
