@@ -247,7 +247,10 @@ __global__ __launch_bounds__(TPB / TPW * kWave) void gate_pair_kernel(
     static_assert(!HIST || TPB == kPairTokens, "a workgroup with counts is one column");
     constexpr int LPT = kWave / TPW;  // lanes per token
     constexpr int LPT_LOG2 = TPW == 1 ? 6 : 5;
-    __shared__ int cnt_lds[HIST ? 2 * kMaxExpertsHist : 1];  // E expert counts, then R rank counts
+    // counts: E expert counts, then R rank counts (LDS atomics); or, with
+    // four experts per lane and R <= 64, rows of per-wavefront counts
+    __shared__ int cnt_lds[HIST ? 2 * kMaxExpertsHist : 1];
+    static_assert(2 * (TPB / TPW) * kWave <= 2 * kMaxExpertsHist, "count rows fit the counters");
     const int k = KF > 0 ? KF : k_rt;
     const int G = GF > 0 ? GF : G_rt;
     // lanes per group: LPT / G when the groups are runs of whole lanes
@@ -260,14 +263,20 @@ __global__ __launch_bounds__(TPB / TPW * kWave) void gate_pair_kernel(
     const int hl = lane & (LPT - 1);             // lane within the token
     const int t0 = blockIdx.x * TPB + wave * TPW;
     if (!HIST && t0 >= T) return;  // the whole wave leaves; nothing below synchronises
-    if (HIST)
+    const bool track_ranks = HIST && R <= 64;
+    // with four experts per lane and the ranks tracked, the counts need no
+    // LDS atomics: each lane adds up the picks of its own four experts as
+    // packed bytes during the pick rounds, and the column sums rows
+    const bool row_counts = EPL == 4 && track_ranks;
+    if (HIST && !row_counts)
         for (int i = threadIdx.x; i < E + R; i += blockDim.x) cnt_lds[i] = 0;
     const bool wlive = t0 < T;  // uniform: this wave has a token
     const int t = t0 + half;
     const bool live = t < T;  // the last wave's second half may have no token
-    const bool track_ranks = HIST && R <= 64;
+    uint32_t cw = 0u;  // byte i: picks of the token's expert 4 * hl + i (four experts per lane)
     int my_e = 0;
     uint64_t first0 = 0, first1 = 0;  // bit j: pick j of the token is its first on that rank
+    uint64_t seen0 = 0, seen1 = 0;  // ranks picked so far, per token
     if (wlive) {
 
     // 1. scores: EPL consecutive logits per lane, 16-byte loads through one
@@ -331,7 +340,6 @@ __global__ __launch_bounds__(TPB / TPW * kWave) void gate_pair_kernel(
 
     uint32_t my_s = 0u;
     float S = 0.0f;
-    uint64_t seen0 = 0, seen1 = 0;  // ranks picked so far, per token
     if constexpr (EPL == 4) {
     // 3-4 with four experts per lane (256 experts at one token per
     // wavefront, 128 at two): each key carries its place in the lane, and the
@@ -418,10 +426,13 @@ __global__ __launch_bounds__(TPB / TPW * kWave) void gate_pair_kernel(
             const uint32_t r0 = rank_of(e0, epr_magic) & 63u;
             first0 |= (uint64_t)(((seen0 >> r0) & 1ull) ^ 1ull) << j;
             seen0 |= 1ull << r0;
+            // the pick's lane (e / 4 of its token's lanes) counts it in byte e % 4
+            cw += lane == (int)(e0 >> 2) ? 1u << ((e0 & 3u) << 3) : 0u;
             if (TPW == 2) {
                 const uint32_t r1 = rank_of(e1, epr_magic) & 63u;
                 first1 |= (uint64_t)(((seen1 >> r1) & 1ull) ^ 1ull) << j;
                 seen1 |= 1ull << r1;
+                cw += lane == 32 + (int)(e1 >> 2) ? 1u << ((e1 & 3u) << 3) : 0u;
             }
         }
     });
@@ -515,11 +526,46 @@ __global__ __launch_bounds__(TPB / TPW * kWave) void gate_pair_kernel(
     }
     }  // wlive
 
+    if constexpr (HIST && EPL == 4) {
+        if (row_counts) {
+            // wavefront w writes row w: its lanes' packed expert counts, and
+            // per rank r < R (lane r) its tokens with a pick on r; a second
+            // half without a token counts nothing
+            constexpr int NW = TPB / TPW;
+            uint32_t rv = 0u;
+            if (wlive) {
+                rv = (uint32_t)((seen0 >> lane) & 1ull);
+                if (TPW == 2 && t0 + 1 < T) rv += (uint32_t)((seen1 >> lane) & 1ull);
+            }
+            cnt_lds[wave * kWave + lane] = (int)(live ? cw : 0u);
+            cnt_lds[(NW + wave) * kWave + lane] = (int)rv;
+            __syncthreads();
+            const size_t c = blockIdx.x;
+            if (wave == 0 && lane < LPT) {
+                // lane w sums word w (experts 4w .. 4w + 3) over the rows and
+                // the halves: byte sums stay <= kPairTokens, so no carries
+                uint32_t sum = 0u;
+#pragma unroll
+                for (int w = 0; w < NW; ++w) {
+                    sum += (uint32_t)cnt_lds[w * kWave + lane];
+                    if (TPW == 2) sum += (uint32_t)cnt_lds[w * kWave + 32 + lane];
+                }
+                reinterpret_cast<uint32_t*>(hist + c * E)[lane] = sum;
+            }
+            if (wave == 1 && lane < R) {
+                int sum = 0;
+#pragma unroll
+                for (int w = 0; w < NW; ++w) sum += cnt_lds[(NW + w) * kWave + lane];
+                rank_hist[c * R + lane] = (uint8_t)sum;
+            }
+            return;
+        }
+    }
     if (HIST) {
         const bool pick = wlive && live && hl < k;
         const int r = pick ? (int)rank_of((uint32_t)my_e, epr_magic) : -1;
         bool first = pick;
-        if (track_ranks) {
+        if (EPL != 4 && track_ranks) {  // (four experts per lane and R <= 64 took the rows above)
             first = pick && (((half ? first1 : first0) >> hl) & 1ull);
         } else {
             // a pick is the token's first on its rank when no earlier pick of

@@ -53,8 +53,10 @@ constexpr int kSelfScanMaxBlocks = 64;
 constexpr long kSmallMaxPairs = 1024;
 constexpr size_t kSmallMaxLds = 65536;
 
-// exclusive block-wide prefix sum; `wsum` is LDS scratch of blockDim/64 ints
-__device__ int block_exclusive_sum(int v, int* total, int* wsum) {
+// exclusive block-wide prefix sum; `wsum` is LDS scratch of blockDim/64 ints.
+// `again`: the caller scans again with the same scratch, so every wavefront
+// must have read it before it returns; a single scan skips that barrier.
+__device__ int block_exclusive_sum(int v, int* total, int* wsum, bool again) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
     const int inc = wave_inclusive_sum(v);
     if (lane == 63) wsum[wave] = inc;
@@ -65,7 +67,7 @@ __device__ int block_exclusive_sum(int v, int* total, int* wsum) {
         pre += (w < wave) ? x : 0;
         tot += x;
     }
-    __syncthreads();
+    if (again) __syncthreads();
     *total = tot;
     return pre + inc - v;
 }
@@ -95,9 +97,12 @@ __global__ __launch_bounds__(512) void layout_count_kernel(const int32_t* __rest
                                                            int R, int EPR, int C) {
     extern __shared__ int32_t cnt_sm[];  // E expert counts, then R rank counts
     const int tid = threadIdx.x;
+    // block c: XCD-contiguous order, so the column entries c of a histogram
+    // row (adjacent ints) are written from one XCD's L2
+    const int c = xcd_item(blockIdx.x, gridDim.x);
     for (int i = tid; i < E + R; i += blockDim.x) cnt_sm[i] = 0;
     __syncthreads();
-    const long p = (long)blockIdx.x * blockDim.x + tid;
+    const long p = (long)c * blockDim.x + tid;
     if (p < P) {
         const int e = idx[p];
         if ((unsigned)e < (unsigned)E) {
@@ -109,7 +114,6 @@ __global__ __launch_bounds__(512) void layout_count_kernel(const int32_t* __rest
         }
     }
     __syncthreads();
-    const int c = blockIdx.x;
     for (int i = tid; i < E; i += blockDim.x) hist[(size_t)i * C + c] = cnt_sm[i];
     for (int i = tid; i < R; i += blockDim.x) rk[(size_t)i * C + c] = cnt_sm[E + i];
 }
@@ -131,7 +135,7 @@ __global__ __launch_bounds__(kScanThreads) void layout_scan_kernel(int32_t* __re
             const int c = c0 + tid;
             const int v = (c < C) ? col[c] : 0;
             int tile;
-            const int ex = block_exclusive_sum(v, &tile, wsum);
+            const int ex = block_exclusive_sum(v, &tile, wsum, true);
             if (c < C) col[c] = carry + ex;
             carry += tile;
         }
@@ -143,7 +147,7 @@ __global__ __launch_bounds__(kScanThreads) void layout_scan_kernel(int32_t* __re
             const int c = c0 + tid;
             const int v = (c < C) ? row[c] : 0;
             int tile;
-            block_exclusive_sum(v, &tile, wsum);
+            block_exclusive_sum(v, &tile, wsum, true);
             sum += tile;
         }
         if (tid == 0) ntok_rank[b - E] = sum;
@@ -156,15 +160,17 @@ __global__ __launch_bounds__(kScanThreads) void layout_scan_kernel(int32_t* __re
 // in an LDS mask per expert (64-bit atomic OR, which commutes), and a pair's
 // rank within its wavefront is the popcount of the mask bits of the lanes
 // before it.  `base[e]` holds the row of the block's first pair with expert
-// e.  Writes slot and recv_token for the pairs below P.
+// e.  Writes slot and recv_token for the pairs below P.  `sync`: wait for
+// the whole block before setting mask bits (needed when the masks were
+// cleared since the block's last barrier).
 template <int W>
 __device__ void assign_pairs(int e, long p0, const int32_t* base, uint64_t* mask, int32_t* wpre,
                              int32_t* __restrict__ slot, int32_t* __restrict__ recv_token, long P, int k, int E,
-                             int total) {
+                             int total, bool sync) {
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     constexpr int NT = W * 64;
     const long p = p0 + tid;
-    __syncthreads();
+    if (sync) __syncthreads();
     if (e >= 0) atomicOr(reinterpret_cast<unsigned long long*>(&mask[wave * E + e]), 1ull << lane);
     __syncthreads();
     for (int i = tid; i < E; i += NT) {
@@ -216,9 +222,10 @@ __device__ __forceinline__ int chunk_expert_global(const int32_t* __restrict__ i
 template <int W>
 __device__ void assign_block(const int32_t* __restrict__ idx, const int32_t* base, uint64_t* mask, int32_t* wpre,
                              int32_t* __restrict__ slot, int32_t* __restrict__ recv_token, long P, int k, int E,
-                             int total, int c) {
+                             int total, int c, bool sync) {
     const long p0 = (long)c * (W * 64);
-    assign_pairs<W>(pair_expert(idx, p0 + threadIdx.x, P, E), p0, base, mask, wpre, slot, recv_token, P, k, E, total);
+    assign_pairs<W>(pair_expert(idx, p0 + threadIdx.x, P, E), p0, base, mask, wpre, slot, recv_token, P, k, E, total,
+                    sync);
 }
 
 template <int W>
@@ -233,7 +240,7 @@ __global__ __launch_bounds__(W * 64) void layout_assign_kernel(
     __shared__ int wsum[W];
 
     const int tid = threadIdx.x;
-    const int c = blockIdx.x;
+    const int c = xcd_item(blockIdx.x, gridDim.x);  // XCD-contiguous, as in layout_assign_cols_kernel
     constexpr int NT = W * 64;
 
     for (int i = tid; i < W * E; i += NT) mask[i] = 0ull;
@@ -245,7 +252,7 @@ __global__ __launch_bounds__(W * 64) void layout_assign_kernel(
     for (int i = 0; i < EPT; ++i)
         if (e0 + i < E) local += cnt[e0 + i];
     int total;
-    int ex = block_exclusive_sum(local, &total, wsum);
+    int ex = block_exclusive_sum(local, &total, wsum, false);
     for (int i = 0; i < EPT; ++i) {
         const int e = e0 + i;
         if (e < E) {
@@ -255,7 +262,7 @@ __global__ __launch_bounds__(W * 64) void layout_assign_kernel(
         }
     }
     if (c == 0 && tid == 0) off[E] = total;
-    assign_block<W>(idx, base, mask, wpre, slot, recv_token, P, k, E, total, c);
+    assign_block<W>(idx, base, mask, wpre, slot, recv_token, P, k, E, total, c, false);
 }
 
 // Assign without a separate scan launch: each block sums the block
@@ -276,7 +283,7 @@ __global__ __launch_bounds__(W * 64) void layout_assign_scan_kernel(
     __shared__ int wsum[W];
 
     const int tid = threadIdx.x;
-    const int c = blockIdx.x;
+    const int c = xcd_item(blockIdx.x, gridDim.x);  // XCD-contiguous, as in layout_assign_cols_kernel
     constexpr int NT = W * 64;
 
     for (int i = tid; i < W * E; i += NT) mask[i] = 0ull;
@@ -310,7 +317,7 @@ __global__ __launch_bounds__(W * 64) void layout_assign_scan_kernel(
     for (int i = 0; i < EPT; ++i)
         if (e0 + i < E) local += tot[e0 + i];
     int total;
-    int ex = block_exclusive_sum(local, &total, wsum);
+    int ex = block_exclusive_sum(local, &total, wsum, false);
     for (int i = 0; i < EPT; ++i) {
         const int e = e0 + i;
         if (e < E) {
@@ -323,7 +330,7 @@ __global__ __launch_bounds__(W * 64) void layout_assign_scan_kernel(
         }
     }
     if (c == 0 && tid == 0) off[E] = total;
-    assign_block<W>(idx, base, mask, wpre, slot, recv_token, P, k, E, total, c);
+    assign_block<W>(idx, base, mask, wpre, slot, recv_token, P, k, E, total, c, false);
 }
 
 // Small inputs in one launch and one workgroup: the P expert ids are
@@ -390,7 +397,7 @@ __global__ __launch_bounds__(W * 64) void layout_small_kernel(
     for (int i = 0; i < EPT; ++i)
         if (e0 + i < E) local += tot[e0 + i];
     int total;
-    int ex = block_exclusive_sum(local, &total, wsum);
+    int ex = block_exclusive_sum(local, &total, wsum, false);
     for (int i = 0; i < EPT; ++i) {
         const int e = e0 + i;
         if (e < E) {
@@ -403,7 +410,7 @@ __global__ __launch_bounds__(W * 64) void layout_small_kernel(
     if (tid == 0) off[E] = total;
     const int C = (int)((P + NT - 1) / NT);
     for (int c = 0; c < C; ++c) {
-        assign_block<W>(ids, base, mask, wpre, slot, recv_token, P, k, E, total, c);
+        assign_block<W>(ids, base, mask, wpre, slot, recv_token, P, k, E, total, c, c > 0);
         __syncthreads();
         // the next chunk's rows start after this chunk's pairs
         for (int i = tid; i < E; i += NT) {
@@ -454,7 +461,11 @@ __global__ __launch_bounds__(W * 64) void layout_assign_cols_kernel(
     int32_t* rtot = red + 2 * W * E;                             // [R]
     __shared__ int wsum[W];
     const int tid = threadIdx.x;
-    const int c0 = blockIdx.x * CB;
+    // XCD-contiguous blocks: an expert's rows from adjacent blocks are
+    // adjacent, so the lines of recv_token (a few rows from each block) are
+    // written from one or two XCDs' L2 instead of all eight (6.36 -> 6.16 us
+    // at 4096 tokens, 256 experts, top-8)
+    const int c0 = xcd_item(blockIdx.x, gridDim.x) * CB;
     const long p_begin = (long)c0 * CT * k;
     const long p_end = min(P, (long)(c0 + CB) * CT * k);
     int e_first = chunk_expert_global(idx, p_begin, p_end, E);
@@ -558,7 +569,7 @@ __global__ __launch_bounds__(W * 64) void layout_assign_cols_kernel(
     for (int i = 0; i < EPT; ++i)
         if (e0 + i < E) local += wpre[e0 + i];
     int total;
-    int ex = block_exclusive_sum(local, &total, wsum);
+    int ex = block_exclusive_sum(local, &total, wsum, false);
     for (int i = 0; i < EPT; ++i) {
         const int e = e0 + i;
         if (e < E) {
@@ -575,7 +586,7 @@ __global__ __launch_bounds__(W * 64) void layout_assign_cols_kernel(
 
     for (long p0 = p_begin; p0 < p_end; p0 += NT) {
         const int e = p0 == p_begin ? e_first : chunk_expert_global(idx, p0, p_end, E);
-        assign_pairs<W>(e, p0, base, mask, wpre, slot, recv_token, p_end, k, E, total);
+        assign_pairs<W>(e, p0, base, mask, wpre, slot, recv_token, p_end, k, E, total, p0 != p_begin);
         if (p0 + NT >= p_end) break;  // (uniform) no next chunk
         __syncthreads();
         // the next chunk's rows start after this chunk's pairs
