@@ -212,7 +212,11 @@ constexpr int kMaxExpertsHist = 1024;
 // = picks of expert e and rank_hist[c][r] = tokens with at least one pick
 // on virtual rank r (its first pick there), as bytes (at most kPairTokens
 // each, since a token's picks are distinct experts).  The layout's assign
-// step sums these columns instead of a separate counting launch.
+// step sums these columns instead of a separate counting launch.  With four
+// experts per lane and R <= 64 each wavefront keeps its counts in registers
+// (packed bytes per lane, ranks as a scalar mask) and the column sums one
+// LDS row per wavefront after a single barrier; other shapes count with LDS
+// atomics.
 //
 // KF, GF: k and G as compile-time constants for common shapes (0: the
 // runtime values), so that the group ranking's lane reads and the pick
@@ -381,25 +385,33 @@ __global__ __launch_bounds__(TPB / TPW * kWave) void gate_pair_kernel(
         v = max(v, dpp_u32<kDppHalfMirror>(v));
         v = max(v, dpp_u32<kDppMirror>(v));
         v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, kDppRowBcast15, 0xA, 0xF, false));
+        // The owner of each token is the lowest lane of its ballot: a token's
+        // lanes hold its maximum key, which passes the test, so neither half
+        // is empty (a half without a token holds zero keys, which all pass).
+        // The owner mask (x & -x per half) is formed on the scalar unit and
+        // used as a lane mask, so no lane comparison waits for the index.
         uint32_t m0, m1 = 0u, hb1 = 0u;
         int o0, o1 = 32;
-        uint64_t eq;
+        uint64_t own;
         if constexpr (TPW == 2) {
             m0 = (uint32_t)__builtin_amdgcn_readlane((int)v, 31);
             m1 = (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
             const uint32_t tgt = m0 ^ ((m0 ^ m1) & hsel);
-            eq = __ballot(q[0] >= (tgt & ~3u));
-            o0 = __ffsll((unsigned long long)(eq & ~kHiHalf)) - 1;
-            o1 = __ffsll((unsigned long long)(eq & kHiHalf)) - 1;
+            const uint64_t eq = __ballot(q[0] >= (tgt & ~3u));
+            const uint64_t lo = eq & ~kHiHalf, hi = eq & kHiHalf;
+            own = (lo & (0ull - lo)) | (hi & (0ull - hi));
+            o0 = __builtin_ctzll(lo);
+            o1 = __builtin_ctzll(hi);
             hb1 = (uint32_t)__builtin_amdgcn_readlane((int)q[0], o1);
         } else {
             v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, kDppRowBcast31, 0xC, 0xF, false));
             m0 = (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
-            eq = __ballot(q[0] >= (m0 & ~3u));
-            o0 = __ffsll((unsigned long long)eq) - 1;
+            const uint64_t eq = __ballot(q[0] >= (m0 & ~3u));
+            own = eq & (0ull - eq);
+            o0 = __builtin_ctzll(eq);
         }
         const uint32_t hb0 = (uint32_t)__builtin_amdgcn_readlane((int)q[0], o0);
-        const bool owner = lane == o0 || (TPW == 2 && lane == o1);
+        const bool owner = __builtin_amdgcn_inverse_ballot_w64(own);
         q[0] = owner ? q[1] : q[0];
         q[1] = owner ? q[2] : q[1];
         q[2] = owner ? q[3] : q[2];
@@ -426,14 +438,18 @@ __global__ __launch_bounds__(TPB / TPW * kWave) void gate_pair_kernel(
             const uint32_t r0 = rank_of(e0, epr_magic) & 63u;
             first0 |= (uint64_t)(((seen0 >> r0) & 1ull) ^ 1ull) << j;
             seen0 |= 1ull << r0;
-            // the pick's lane (e / 4 of its token's lanes) counts it in byte e % 4
-            cw += lane == (int)(e0 >> 2) ? 1u << ((e0 & 3u) << 3) : 0u;
+            // the owner lane holds the pick (expert e = 4 * lane + e % 4 of
+            // its token) and counts it in byte e % 4
+            const uint32_t inc0 = 1u << ((e0 & 3u) << 3);
+            uint32_t inc = inc0;
             if (TPW == 2) {
                 const uint32_t r1 = rank_of(e1, epr_magic) & 63u;
                 first1 |= (uint64_t)(((seen1 >> r1) & 1ull) ^ 1ull) << j;
                 seen1 |= 1ull << r1;
-                cw += lane == 32 + (int)(e1 >> 2) ? 1u << ((e1 & 3u) << 3) : 0u;
+                const uint32_t inc1 = 1u << ((e1 & 3u) << 3);
+                inc = inc0 ^ ((inc0 ^ inc1) & hsel);
             }
+            cw += owner ? inc : 0u;
         }
     });
     if constexpr (KF > 0) {
