@@ -5,14 +5,16 @@ and ep_get_layout calls. Shapes: every workload; random shapes of the pair
 gate (E in {128, 256, 512, 1024}, groups of whole lanes or every group kept,
 m <= 2, k up to 32, any R) at token counts around the 16-token columns and
 the 64-token assign blocks, with normal and tie-heavy logits; the assign
-launch's lane strides; one and two tokens per wavefront around 4096 tokens
-(top-6 keeps the switch, top-8 of 8 groups stays at one); and shapes that
-take the fallback path (among them E = 512 and 1024, whose assign launch
-would need more than 64 KiB of LDS, and E with a count of experts per
-lane that is not a power of two: 160, 192, 320, 384, 640 and 768); exact
-score ties for the pick rounds of 256 experts, four per lane; logits only
-4-byte aligned; and NaN logits (outside the contract: k distinct experts
-in range per token, the other tokens as the oracle routes them)."""
+launch's lane strides; the routing launch's two ways of counting
+(per-wavefront rows, LDS atomics) at their edges; one and two tokens per
+wavefront around 4096 tokens (top-6 keeps the switch, top-8 of 8 groups
+stays at one); and shapes that take the fallback path (among them E = 512
+and 1024, whose assign launch would need more than 64 KiB of LDS, and E with
+a count of experts per lane that is not a power of two: 160, 192, 320, 384,
+640 and 768); exact score ties for the pick rounds of 256 experts, four per
+lane; logits only 4-byte aligned; and NaN logits (outside the contract: k
+distinct experts in range per token, the other tokens as the oracle routes
+them)."""
 import numpy as np
 import pytest
 import torch
@@ -168,6 +170,22 @@ def test_route_layout_column_reduction_strides(E, G):
     assert _two_launch(w)
     say("route_layout strides", w)
     check(w, W.gen_logits(w))
+
+
+@pytest.mark.parametrize("E,G,R,T", [
+    (128, 8, 64, 4095), (128, 4, 32, 1023), (128, 8, 128, 2049), (128, 8, 1, 129),
+    (256, 8, 64, 4081), (256, 8, 128, 1031), (256, 16, 2, 200),
+])
+def test_route_layout_count_rows_and_atomics(E, G, R, T):
+    # the routing launch counts its picks per column in per-wavefront rows
+    # when each lane holds four experts and R <= 64, else with LDS atomics:
+    # odd T at 128 experts leaves the last wavefront's upper half without a
+    # token, and T off a multiple of 16 leaves tokenless wavefronts in the
+    # last column
+    w = W.Workload("rows", T=T, H=128, E=E, G=G, TG=G // 2, k=8, R=R, m=2, seed=E * 7 + R + T)
+    assert _two_launch(w)
+    say("route_layout count rows", w)
+    check(w, W.gen_logits(w), with_recv_token=True)
 
 
 @pytest.mark.parametrize("T,k", [(4095, 8), (4096, 8), (4097, 8), (6000, 8), (4096, 6), (4097, 6), (6000, 6)])
