@@ -17,9 +17,11 @@ line also reports the step replayed from a captured HIP graph that holds
 one step per buffer set (`graph_step_us`), which removes the host's launch
 gaps.
 
-Prints one JSON line.  `value` is dispatch+combine algorithmic bytes divided
-by the summed average durations of the dispatch and combine kernels, from
-HIP events recorded on the launch stream over the timed steps.  The
+Prints one JSON line.  `ms_per_step` is the wall time of the timed steps,
+which hold nothing but the step's own calls.  `value` is dispatch+combine
+algorithmic bytes divided by the summed average durations of the dispatch
+and combine kernels, from HIP events recorded on the launch stream around
+each stage in as many further steps (the buffer sets keep rotating).  The
 `roofline` object reports the dominant kernel (combine); `cpu_baseline`
 times the CPU oracle on the same batch, on one thread and on every thread
 the process may use, and `parity` compares its outputs with the GPU's.
@@ -298,9 +300,12 @@ HEADLINE_METRIC = "dispatch+combine HBM GB/s and % of peak at 4096 tok x 7168 hi
 
 
 def timed_steps(args, nsets, launch_stages, stages):
-    """Runs `warmup` untimed and `steps` timed steps; each step calls
-    launch_stages(set_index, record) which records an event before each stage
-    and one after the last.  Returns (per-stage durations in seconds, wall
+    """Runs `warmup` untimed steps, then `steps` timed steps with nothing
+    inside them but the step's own calls (the wall clock between two
+    synchronisations gives the step time), then `steps` more in which
+    launch_stages(set_index, record) records an event before each stage and
+    one after the last (the per-stage durations).  The buffer sets rotate
+    through all three runs.  Returns (per-stage durations in seconds, wall
     seconds of the timed steps)."""
     import torch
     hev = HipEvents()
@@ -310,13 +315,16 @@ def timed_steps(args, nsets, launch_stages, stages):
     for i, ev in enumerate(warm):
         launch_stages(i % nsets, lambda q, ev=ev: hev.record(ev[q], sh))
     torch.cuda.synchronize()
-    evs = [hev.create(n) for _ in range(args.steps)]
-    torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i, ev in enumerate(evs):
-        launch_stages((args.warmup + i) % nsets, lambda q, ev=ev: hev.record(ev[q], sh))
+    for i in range(args.steps):
+        launch_stages((args.warmup + i) % nsets, lambda q: None)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    evs = [hev.create(n) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for i, ev in enumerate(evs):
+        launch_stages((args.warmup + args.steps + i) % nsets, lambda q, ev=ev: hev.record(ev[q], sh))
+    torch.cuda.synchronize()
     dur = {s: [hev.seconds(ev[i], ev[i + 1]) for ev in evs] for i, s in enumerate(stages)}
     for ev in warm + evs:
         hev.destroy(ev)
