@@ -558,7 +558,9 @@ __global__ __launch_bounds__(W * 64) void layout_assign_cols_kernel(
         base[e] = before;
         wpre[e] = all;
     }
-    __syncthreads();
+    // with E <= NT the scan below reads only the expert each thread summed
+    // (thread e), so only a wider E needs the block to wait here
+    if (E > NT) __syncthreads();
     if (blockIdx.x == 0)
         for (int i = tid; i < R; i += NT) ntok_rank[i] = rtot[i];
 
