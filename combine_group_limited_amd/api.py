@@ -12,7 +12,9 @@ stream has finished (for example until a synchronisation), as the C ABI
 requires: torch's caching allocator only orders reuse of freed memory on
 the current stream.  (Tensor.record_stream is no substitute for streams the
 caller destroys, such as CuRangeStream: the allocator would later record
-events on the destroyed stream.)
+events on the destroyed stream.)  A layout call that allocates its own
+workspace returns it in its dict under "workspace" for that reason: the
+kernels on `stream` may still use it after the call returns.
 """
 from __future__ import annotations
 
@@ -129,7 +131,8 @@ def layout_workspace_bytes(cfg: Config) -> int:
 def get_layout(cfg: Config, topk_idx: torch.Tensor, out: dict | None = None, workspace=None,
                with_recv_token: bool = True, stream=None) -> dict:
     """Routing layout. Returns dict with cnt [E], ntok_rank [R], off [E+1],
-    slot [T, k] and (if requested) recv_token [T*k], all int32."""
+    slot [T, k] and (if requested) recv_token [T*k], all int32, and the
+    workspace when the call allocated it."""
     dev = topk_idx.device
     _want(topk_idx, "topk_idx", (cfg.T, cfg.k), torch.int32, None)
     o = dict(out or {})
@@ -149,7 +152,7 @@ def get_layout(cfg: Config, topk_idx: torch.Tensor, out: dict | None = None, wor
         _want(rt, "recv_token", (cfg.T * cfg.k,), torch.int32, dev)
     need = layout_workspace_bytes(cfg)
     if workspace is None:
-        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+        workspace = o["workspace"] = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
     if workspace.dtype != torch.uint8 or workspace.device != dev or not workspace.is_contiguous():
         raise ValueError("workspace must be a contiguous uint8 tensor on %s" % dev)
     c = cfg.c()
@@ -168,7 +171,8 @@ def route_layout(cfg: Config, logits: torch.Tensor, out: dict | None = None, wor
                  with_recv_token: bool = True, stream=None) -> dict:
     """route followed by get_layout, in fewer launches, with the same
     results: a dict with idx [T, k] int32, w [T, k] fp32 and the layout's
-    cnt, ntok_rank, off, slot and (if requested) recv_token."""
+    cnt, ntok_rank, off, slot and (if requested) recv_token, and the
+    workspace when the call allocated it."""
     dev = logits.device
     _want(logits, "logits", (cfg.T, cfg.E), torch.float32, None)
     o = dict(out or {})
@@ -192,7 +196,7 @@ def route_layout(cfg: Config, logits: torch.Tensor, out: dict | None = None, wor
         _want(rt, "recv_token", (cfg.T * cfg.k,), torch.int32, dev)
     need = route_layout_workspace_bytes(cfg)
     if workspace is None:
-        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+        workspace = o["workspace"] = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
     if workspace.dtype != torch.uint8 or workspace.device != dev or not workspace.is_contiguous():
         raise ValueError("workspace must be a contiguous uint8 tensor on %s" % dev)
     c = cfg.c()
@@ -354,9 +358,9 @@ def rank_layout_workspace_bytes(cfg: Config) -> int:
 def get_rank_layout(cfg: Config, topk_idx: torch.Tensor, out: dict | None = None, workspace=None,
                     with_rank_token: bool = True, stream=None) -> dict:
     """Per-rank deduplicated layout: dict with rank_count [R], rank_offset
-    [R+1], rank_slot [T, k] and (if requested) rank_token [T*k], all int32.
-    ep_dispatch with rank_slot as the slot map is the deduplicated
-    dispatch."""
+    [R+1], rank_slot [T, k] and (if requested) rank_token [T*k], all int32,
+    and the workspace when the call allocated it.  ep_dispatch with
+    rank_slot as the slot map is the deduplicated dispatch."""
     dev = topk_idx.device
     _want(topk_idx, "topk_idx", (cfg.T, cfg.k), torch.int32, None)
     o = dict(out or {})
@@ -374,7 +378,7 @@ def get_rank_layout(cfg: Config, topk_idx: torch.Tensor, out: dict | None = None
         _want(rt, "rank_token", (cfg.T * cfg.k,), torch.int32, dev)
     need = rank_layout_workspace_bytes(cfg)
     if workspace is None:
-        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+        workspace = o["workspace"] = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
     if workspace.dtype != torch.uint8 or workspace.device != dev or not workspace.is_contiguous():
         raise ValueError("workspace must be a contiguous uint8 tensor on %s" % dev)
     c = cfg.c()

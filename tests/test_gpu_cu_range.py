@@ -1,11 +1,13 @@
 """The library's calls on streams confined to a range of compute units
 (ep_stream_create_cu_range, the CU-budget analogue of the pages' SM-count
-control) against the CPU oracle: the normal path (route, layout, FP8
-dispatch, combine), the low-latency path (dispatch_ll, combine_ll) and the
+control) against the CPU oracle: the normal path (route, layout, the
+routing with its layout in two launches, FP8 dispatch, combine), the
+low-latency path (dispatch_ll, combine_ll) and the
 deduplicated path (rank layout, dispatch over rank slots, in-rank partial
 combine, combine of partials), bit for bit (flat combines within 1 bf16
 ulp).  Every device input is created before the calls and kept until the
-stream has been synchronised."""
+stream has been synchronised; the layout calls' own workspaces come back
+with their outputs and are kept as long."""
 import numpy as np
 import pytest
 import torch
@@ -72,6 +74,7 @@ def run_on(stream, w, cfg, d, cap):
     """All three paths on `stream`; returns host copies of every output."""
     idx, wt = ep.route(cfg, d["lg"], stream=stream)
     lay = ep.get_layout(cfg, idx, stream=stream)
+    fused = ep.route_layout(cfg, d["lg"], stream=stream)
     recv, sc = ep.dispatch(cfg, d["x"], lay["slot"], stream=stream)
     out = ep.combine(cfg, d["y"], lay["slot"], wt, stream=stream)
     nll = w.E * cap
@@ -89,8 +92,9 @@ def run_on(stream, w, cfg, d, cap):
     torch.cuda.synchronize()
     g = dict(idx=idx, wt=wt, recv=recv, sc=sc, out=out, ll_slot=ll["slot"], ll_count=ll["count"],
              ll_recv=ll_recv, ll_sc=ll_sc, ll_out=ll_out, rk_recv=rk_recv, rk_sc=rk_sc, part=part, rk_out=rk_out)
-    g.update(lay)
-    g.update(rl)
+    g.update({k: v for k, v in lay.items() if k != "workspace"})
+    g.update({k: v for k, v in rl.items() if k != "workspace"})
+    g.update({"fused_" + k: v for k, v in fused.items() if k != "workspace"})
     return {k: to_host(v) for k, v in g.items()}
 
 
@@ -115,5 +119,9 @@ def test_cu_range_streams_match_oracle():
                     "ll_slot", "ll_count", "ll_recv", "ll_sc", "rank_count", "rank_offset", "rank_slot",
                     "rank_token", "rk_recv", "rk_sc", "part", "rk_out"):
             same(key, g[key], e[key])
+        for key in ("cnt", "off", "ntok_rank", "slot", "recv_token"):
+            same("route_layout " + key, g["fused_" + key], e[key])
+        same("route_layout idx", g["fused_idx"], e["idx"])
+        same("route_layout w", g["fused_w"], e["wt"])
         within_ulp("combine", g["out"], e["out"])
         within_ulp("combine_ll", g["ll_out"], e["ll_out"])
