@@ -438,8 +438,8 @@ __global__ __launch_bounds__(TPB / TPW * kWave) void gate_pair_kernel(
             const uint32_t r0 = rank_of(e0, epr_magic) & 63u;
             first0 |= (uint64_t)(((seen0 >> r0) & 1ull) ^ 1ull) << j;
             seen0 |= 1ull << r0;
-            // the owner lane holds the pick (expert e = 4 * lane + e % 4 of
-            // its token) and counts it in byte e % 4
+            // the owner lane holds the pick (expert e = 4 * hl + e % 4 of its
+            // token, hl its lane within the token) and counts it in byte e % 4
             const uint32_t inc0 = 1u << ((e0 & 3u) << 3);
             uint32_t inc = inc0;
             if (TPW == 2) {
