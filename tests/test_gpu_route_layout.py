@@ -276,3 +276,24 @@ def test_nan_logits_still_give_distinct_picks(w):
         assert all(len(set(row)) == w.k for row in gi.tolist()), name + ": repeated expert"
         assert np.array_equal(gi[ok], oi), name + ": tokens without NaN"
     assert np.array_equal(to_host(got["w"])[ok].view(np.uint32), ow.view(np.uint32))
+
+
+def test_layout_calls_return_the_workspace_they_allocate():
+    # a workspace the call allocates comes back with its outputs (so that it
+    # lives as long as they do, also for work on another stream); one the
+    # caller passes does not
+    w = W.PREFILL.replace(name="ws", T=300, seed=5)
+    cfg = ep.Config.of(w)
+    d = to_dev(W.gen_logits(w))
+    calls = (
+        (lambda ws=None: ep.route_layout(cfg, d, workspace=ws), ep.route_layout_workspace_bytes(cfg)),
+        (lambda ws=None: ep.get_layout(cfg, ep.route(cfg, d)[0], workspace=ws), ep.layout_workspace_bytes(cfg)),
+        (lambda ws=None: ep.get_rank_layout(cfg, ep.route(cfg, d)[0], workspace=ws),
+         ep.rank_layout_workspace_bytes(cfg)),
+    )
+    for call, need in calls:
+        got = call()
+        assert got["workspace"].dtype == torch.uint8 and got["workspace"].numel() >= need
+        mine = torch.empty(max(need, 256), dtype=torch.uint8, device="cuda")
+        assert "workspace" not in call(mine)
+    torch.cuda.synchronize()
