@@ -128,6 +128,9 @@ def parse():
     ap.add_argument("--ceiling-probe", action="store_true",
                     help="HBM rates of plain kernels (streaming read, write, copy; combine- and dispatch-shaped "
                          "copies without their arithmetic) beside the library's dispatch and combine")
+    ap.add_argument("--launch-probe", action="store_true",
+                    help="fixed launch costs in the routing, layout and combine launch shapes, and the routing "
+                         "kernel's memory pattern without its arithmetic, beside ep_route and ep_route_layout")
     return ap.parse_args()
 
 
@@ -292,6 +295,86 @@ def ceiling_probe(args):
     print(json.dumps({"metric": "HBM ceiling probes (plain kernels) beside dispatch and combine, prefill shape",
                       "unit": "GB/s", "peak": HBM_PEAK_GBS, "steps": n,
                       "config": {"workload": w.name, "tokens": w.T, "hidden": w.H, "topk": w.k},
+                      "probes": res}), flush=True)
+    return 0
+
+
+def launch_probe(args):
+    """Fixed costs beside the routing and layout kernels (libhbmprobe.so): a
+    launch that does nothing, in the shapes of the routing launch with column
+    counts (256 workgroups of 1024 threads, 8 KiB of LDS), of the routing
+    launch without them (1024 of 256), of the layout's assign launch (64 of
+    512, its 42 KiB of LDS) and of the combine (57344 one-wave workgroups);
+    the routing kernel's memory pattern without its arithmetic (one wavefront
+    per token reads the token's 256 fp32 logits and writes 8 words to each
+    of two [T, k] outputs) at 16 and 4 tokens per workgroup; and beside them
+    ep_route and ep_route_layout, at the prefill shape.  A 512 MiB fill
+    through the caches before each launch puts the logits back in HBM.  HIP
+    events around each launch; the median over `steps` launches."""
+    import torch
+
+    import combine_group_limited_amd as ep
+    from combine_group_limited_amd import _lib as L
+    from combine_group_limited_amd import build as B
+    import workloads as W
+
+    if not os.path.exists(B.PROBE_LIB_PATH):
+        B.build()
+    P = ctypes.CDLL(B.PROBE_LIB_PATH)
+    vp, i, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+    P.hbm_probe_empty.argtypes = [i, i, sz, vp]
+    P.hbm_probe_token_rows.argtypes = [vp, vp, vp, i, i, i, i, vp]
+    lib = L.lib()
+    dev = torch.device("cuda", 0)
+    sh = int(torch.cuda.current_stream().cuda_stream)
+    w = W.PREFILL
+    cfg = ep.Config.of(w)
+    c = cfg.c()
+    cp = ctypes.byref(c)
+    lg = torch.from_numpy(W.gen_logits(w)).to(dev)
+    o = ep.route_layout(cfg, lg)
+    ws = o["workspace"]
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    o1 = torch.empty((w.T, w.k), dtype=torch.int32, device=dev)
+    o2 = torch.empty((w.T, w.k), dtype=torch.int32, device=dev)
+    torch.cuda.synchronize()
+    hev = HipEvents()
+    n = max(args.steps, 3)
+    assign_lds = (12 * 8 + 4) * w.E + 2 * 8 * w.E * 4 + 4 * w.R
+    probes = {
+        "empty_256x1024_8KiB": lambda: P.hbm_probe_empty(256, 1024, 8192, sh),
+        "empty_1024x256": lambda: P.hbm_probe_empty(1024, 256, 0, sh),
+        "empty_64x512_%dB" % assign_lds: lambda: P.hbm_probe_empty(64, 512, assign_lds, sh),
+        "empty_57344x64": lambda: P.hbm_probe_empty(57344, 64, 0, sh),
+        "token_rows_16_per_wg": lambda: P.hbm_probe_token_rows(lg.data_ptr(), o1.data_ptr(), o2.data_ptr(), w.T, w.E,
+                                                               w.k, 16, sh),
+        "token_rows_4_per_wg": lambda: P.hbm_probe_token_rows(lg.data_ptr(), o1.data_ptr(), o2.data_ptr(), w.T, w.E,
+                                                              w.k, 4, sh),
+        "ep_route": lambda: lib.ep_route(cp, lg.data_ptr(), o["idx"].data_ptr(), o["w"].data_ptr(), sh),
+        "ep_route_layout": lambda: lib.ep_route_layout(cp, lg.data_ptr(), o["idx"].data_ptr(), o["w"].data_ptr(),
+                                                       o["cnt"].data_ptr(), o["ntok_rank"].data_ptr(),
+                                                       o["off"].data_ptr(), o["slot"].data_ptr(),
+                                                       o["recv_token"].data_ptr(), ws.data_ptr(), ws.numel(), sh),
+    }
+    res = {}
+    for name, fn in probes.items():
+        if fn() != 0:
+            raise RuntimeError("probe %s failed" % name)
+        ts = []
+        for j in range(n):
+            flush.fill_(j & 0xFF)
+            e = hev.create(2)
+            hev.record(e[0], sh)
+            fn()
+            hev.record(e[1], sh)
+            ts.append(hev.seconds(e[0], e[1]))
+            hev.destroy(e)
+        ts.sort()
+        res[name] = {"median_us": round(ts[len(ts) // 2] * 1e6, 2), "p10_us": round(ts[len(ts) // 10] * 1e6, 2)}
+        print("probe %-28s %7.2f us" % (name, ts[len(ts) // 2] * 1e6), file=sys.stderr, flush=True)
+    print(json.dumps({"metric": "launch floors and the routing kernel's memory pattern beside routing and layout",
+                      "unit": "us", "steps": n,
+                      "config": {"workload": w.name, "tokens": w.T, "experts": w.E, "topk": w.k},
                       "probes": res}), flush=True)
     return 0
 
@@ -857,6 +940,8 @@ def main():
         return copy_probe()
     if args.ceiling_probe:
         return ceiling_probe(args)
+    if args.launch_probe:
+        return launch_probe(args)
 
     import torch
     import workloads as W

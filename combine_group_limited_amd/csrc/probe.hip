@@ -18,6 +18,12 @@
 //    to each of the k rows rows[t*k + j] of an H-byte-per-row buffer (nt).
 //    The dispatch's scale stores (4 bytes per 128 channels per row) are
 //    left out.
+//  hbm_probe_empty: a launch that does nothing, in a given grid, workgroup
+//    size and LDS allocation: the fixed cost of a launch of that shape.
+//  hbm_probe_token_rows: the routing kernel's memory pattern without its
+//    arithmetic: one wavefront per token (tokens_per_block per workgroup)
+//    reads the token's E fp32 logits with 16-byte loads and writes k words
+//    to each of two [T, k] outputs.
 // Every access goes through a buffer resource sized to its buffer or row,
 // so nothing outside them is touched.
 #include <hip/hip_runtime.h>
@@ -145,6 +151,26 @@ __global__ __launch_bounds__(64, 8) void probe_scatter_kernel(const uint16_t* __
     }
 }
 
+__global__ void probe_empty_kernel() {}
+
+__global__ __launch_bounds__(1024) void probe_token_rows_kernel(const float* __restrict__ logits,
+                                                                uint32_t* __restrict__ o1, uint32_t* __restrict__ o2,
+                                                                int T, int E, int k, int tpb) {
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int t = blockIdx.x * tpb + wave;
+    if (t >= T) return;
+    const auto rr = buffer_rsrc(logits + (size_t)t * E, (uint32_t)E * 4u);
+    uint32_t acc = 0u;
+    for (int i = lane * 4; i < E; i += 256) {
+        const i32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rr, i * 4, 0, kCached);
+        acc ^= (uint32_t)(v.x ^ v.y ^ v.z ^ v.w);
+    }
+    if (lane < k) {
+        o1[(size_t)t * k + lane] = acc;
+        o2[(size_t)t * k + lane] = acc + 1u;
+    }
+}
+
 int grid_for(uint32_t bytes) {
     const uint32_t per_block = kThreads * kU * 16;
     const uint32_t blocks = (bytes + per_block - 1) / per_block;
@@ -208,6 +234,26 @@ __attribute__((visibility("default"))) int hbm_probe_scatter(const void* x, cons
     hipLaunchKernelGGL(probe_scatter_kernel, dim3(items < (1 << 20) ? items : (1 << 20)), dim3(64), 0,
                        static_cast<hipStream_t>(stream), static_cast<const uint16_t*>(x), rows,
                        static_cast<uint8_t*>(recv), H, k, nrows, segs, items);
+    return (int)hipGetLastError();
+}
+
+// grid of `blocks` workgroups of `threads` (a multiple of 64, <= 1024) with
+// `lds` bytes of LDS (<= 64 KiB)
+__attribute__((visibility("default"))) int hbm_probe_empty(int blocks, int threads, size_t lds, void* stream) {
+    if (blocks < 1 || threads < 64 || threads > 1024 || threads % 64 || lds > 65536) return -1;
+    hipLaunchKernelGGL(probe_empty_kernel, dim3(blocks), dim3(threads), lds, static_cast<hipStream_t>(stream));
+    return (int)hipGetLastError();
+}
+
+// logits [T, E] fp32 (E a multiple of 4), o1 and o2 [T, k] words
+__attribute__((visibility("default"))) int hbm_probe_token_rows(const float* logits, uint32_t* o1, uint32_t* o2, int T,
+                                                                int E, int k, int tokens_per_block, void* stream) {
+    if (!logits || !o1 || !o2 || T < 1 || E < 4 || E % 4 || E > 4096 || k < 1 || k > 64 || tokens_per_block < 1 ||
+        tokens_per_block > 16)
+        return -1;
+    const int blocks = (T + tokens_per_block - 1) / tokens_per_block;
+    hipLaunchKernelGGL(probe_token_rows_kernel, dim3(blocks), dim3(64 * tokens_per_block), 0,
+                       static_cast<hipStream_t>(stream), logits, o1, o2, T, E, k, tokens_per_block);
     return (int)hipGetLastError();
 }
 
