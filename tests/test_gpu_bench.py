@@ -2,7 +2,9 @@
 of every path carries the fields its JSON line promises (metric, value,
 unit, steps, ms_per_step, config, ...; the normal path also its roofline,
 CPU baseline, input provenance and parity record), and the normal path's
-own parity check of its buffer set 0 against the oracle passes."""
+own parity check of its buffer set 0 against the oracle passes; the launch
+probe runs and reports every probe."""
+import json
 import os
 import sys
 
@@ -86,3 +88,16 @@ def test_overlap_record():
     rec = bench.run_overlap(a, W.TINY)
     assert rec["budgets"] and rec["budgets"][0]["comm_cus"] == 32
     assert rec["value"] > 0 and rec["full_gpu"]["dc_us"] > 0
+
+
+def test_launch_probe_record(capsys):
+    # the launch floors and the routing kernel's memory pattern, beside
+    # ep_route and ep_route_layout, at the prefill shape
+    say("bench launch probe")
+    assert bench.launch_probe(args_for("--launch-probe", "--steps", "3")) == 0
+    rec = json.loads(capsys.readouterr().out.strip().splitlines()[-1])
+    names = set(rec["probes"])
+    for key in ("empty_256x1024_8KiB", "empty_1024x256", "empty_57344x64", "token_rows_16_per_wg",
+                "token_rows_4_per_wg", "ep_route", "ep_route_layout"):
+        assert key in names, key
+    assert all(v["median_us"] > 0 for v in rec["probes"].values())
